@@ -1,0 +1,77 @@
+"""Comparison rules between the GPU path and the oracle (test infrastructure).
+
+Selection rule: the oracle ranks blocks by the fp64 modulated score m; let
+m_k be the k_eff-th largest m of a row.  Every block whose m lies more than
+GAP away from m_k must have the same membership on both sides; blocks within
+GAP of m_k are exempt (their order can flip under fp32 rounding of the pooled
+sums), but the GPU list must still be valid: exactly k_eff distinct,
+ascending, in-range ids containing every current-chunk block, padded with -1.
+
+Attention rule (bf16 inputs, fp32 accumulation): max |out - ref| <= 2e-2 and
+mean |out - ref| <= 2e-3 against the oracle fed the same block lists; float32
+inputs: 1e-4 / 1e-5.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GAP = 1e-4
+BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3
+F32_MAX_ABS, F32_MEAN_ABS = 1e-4, 1e-5
+
+
+def check_list_valid(kv_idx: np.ndarray, kv_cnt: np.ndarray, nk: int, k_eff: int, cur_first: int):
+    """Structural validity of GPU lists: count, range, strict ascent, padding, current blocks kept."""
+    kv_idx = kv_idx.reshape(-1, kv_idx.shape[-1])
+    kv_cnt = kv_cnt.reshape(-1)
+    assert np.all(kv_cnt == k_eff), f"kv_cnt != {k_eff}: {np.unique(kv_cnt)}"
+    head = kv_idx[:, :k_eff]
+    assert head.min() >= 0 and head.max() < nk, "block id out of range"
+    if k_eff > 1:
+        assert np.all(np.diff(head, axis=1) > 0), "list not strictly ascending"
+    assert np.all(kv_idx[:, k_eff:] == -1), "padding must be -1"
+    ncur = nk - cur_first
+    if ncur > 0:
+        assert np.all(head[:, k_eff - ncur:] == np.arange(cur_first, nk)[None, :]), \
+            "current-chunk blocks must all be kept"
+
+
+def check_selection(gpu_idx: np.ndarray, gpu_cnt: np.ndarray, m: np.ndarray, kth: np.ndarray,
+                    oracle_idx: np.ndarray, k_eff: int, cur_first: int, gap: float = GAP) -> dict:
+    """Gap rule; returns {'rows': n, 'rows_differing': n_in_band_swaps, 'exempt_blocks': n}."""
+    nk = m.shape[-1]
+    m = m.reshape(-1, nk)
+    kth = kth.reshape(-1)
+    gpu_idx = gpu_idx.reshape(m.shape[0], -1)
+    oracle_idx = oracle_idx.reshape(m.shape[0], -1)
+    check_list_valid(gpu_idx, gpu_cnt, nk, k_eff, cur_first)
+    rows = m.shape[0]
+    gpu_mask = np.zeros((rows, nk), bool)
+    ora_mask = np.zeros((rows, nk), bool)
+    r = np.repeat(np.arange(rows), k_eff)
+    gpu_mask[r, gpu_idx[:, :k_eff].reshape(-1)] = True
+    ora_mask[r, oracle_idx[:, :k_eff].reshape(-1)] = True
+    inf_rows = np.isinf(kth) & (kth > 0)
+    if inf_rows.any():
+        assert np.array_equal(gpu_mask[inf_rows], ora_mask[inf_rows]), "k = ncur rows must match exactly"
+    with np.errstate(invalid="ignore"):
+        far = np.abs(m - kth[:, None]) > gap
+    bad = far & (gpu_mask != ora_mask)
+    if bad.any():
+        rr, jj = np.nonzero(bad)
+        msg = [f"row {a} block {b}: m={m[a, b]!r} kth={kth[a]!r} gpu={gpu_mask[a, b]} oracle={ora_mask[a, b]}"
+               for a, b in list(zip(rr, jj))[:8]]
+        raise AssertionError(f"{bad.sum()} out-of-band membership mismatches:\n" + "\n".join(msg))
+    differing = int(np.any(gpu_mask != ora_mask, axis=1).sum())
+    return dict(rows=rows, rows_differing=differing, exempt_blocks=int((~far).sum()))
+
+
+def check_close(out: np.ndarray, ref: np.ndarray, max_abs: float, mean_abs: float, what: str = "out"):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite values"
+    err = np.abs(out - ref)
+    mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3g} (<= {max_abs}), mean-abs {mn:.3g} (<= {mean_abs})"
+    return mx, mn

@@ -1,0 +1,298 @@
+"""Pins of the CPU oracle against facts fixed outside it (closed forms, worked
+examples, brute force, invariants).  No GPU; every check uses only oracle/."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import velox_oracle as O
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, get_config, make_inputs
+from tests.parity_rules import check_selection
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    return math.inf if x == "inf" else float(x)
+
+
+# ---------------------------------------------------------------- pooling
+
+def test_pool_constant_block_is_exact():
+    # a block whose tokens all hold the same vector pools to that vector exactly
+    rng = np.random.default_rng(0)
+    consts = f32_to_bf16_bits(rng.standard_normal((3, 1, 16)).astype(np.float32))
+    x = np.repeat(consts, 64, axis=1).reshape(3 * 64, 16)
+    out = O.pool(x, 64)
+    assert np.array_equal(out, bf16_bits_to_f32(consts[:, 0, :]).astype(np.float64))
+
+
+def test_pool_closed_form_ramp():
+    # x[t, e] = (t mod blk) + e/2  ->  mean over a block = (blk-1)/2 + e/2 exactly
+    blk, d, nb = 8, 6, 5
+    t = np.arange(nb * blk) % blk
+    x = (t[:, None] + 0.5 * np.arange(d)[None, :]).astype(np.float32)
+    x[blk:2 * blk] += 10.0           # block 1 shifted by 10: catches a wrong block stride
+    out = O.pool(x, blk)
+    expect = (blk - 1) / 2 + 0.5 * np.arange(d)[None, :] + np.zeros((nb, 1))
+    expect[1] += 10.0
+    assert np.array_equal(out, expect)
+
+
+# ---------------------------------------------------------------- scores
+
+def test_score_blk1_is_token_logit():
+    # blk = 1: the pooled score reduces to the attention logit q.k/sqrt(d); d = 4 -> /2
+    q = np.array([[[[1, 2, 3, 4]]]], np.float32)
+    k = np.array([[[[1, 1, 1, 1], [-1, 0, 2, 0.5], [0, 0, 0, 0]]]], np.float32)
+    s = O.scores(O.pool(q, 1), O.pool(k, 1))
+    assert s.shape == (1, 1, 1, 3)
+    assert np.array_equal(s[0, 0, 0], [5.0, 3.5, 0.0])
+
+
+def test_score_constant_blocks_closed_form():
+    # Q block constant a, K block j constant b_j -> s_j = a.b_j / sqrt(d) (d = 16 -> /4)
+    d, blk = 16, 4
+    a = np.zeros(d, np.float32); a[0], a[3] = 2.0, -1.0
+    b0 = np.zeros(d, np.float32); b0[0] = 1.0
+    b1 = np.zeros(d, np.float32); b1[3] = 1.0
+    q = np.tile(a, (blk, 1))[None, None]
+    k = np.concatenate([np.tile(b0, (blk, 1)), np.tile(b1, (blk, 1))])[None, None]
+    s = O.scores(O.pool(q, blk), O.pool(k, blk))
+    assert np.array_equal(s[0, 0, 0], [0.5, -0.25])
+
+
+# ---------------------------------------------------------------- modulation + selection, worked examples
+
+def _one_row(s, overlap, covered, alpha, k, C):
+    # blk = T: one block per chunk, so chunk(j) = j and block C is the current chunk
+    s = np.asarray(s, np.float64).reshape(1, 1, 1, -1)
+    ov = np.asarray(overlap, np.float32).reshape(1, 1, C)
+    cov = np.array([[covered]], np.uint8)
+    m = O.modulate(s, ov, cov, blk=1, T=1, alpha=alpha)
+    idx, cnt, kth = O.select(m, k)
+    return m[0, 0, 0], idx[0, 0, 0], int(cnt[0, 0, 0])
+
+
+@pytest.mark.parametrize("name", ["ex1_modulation_changes_set.json", "ex2_literal_sign.json"])
+def test_worked_examples(name):
+    g = golden(name)
+    for case, cov in (("covered", 1), ("uncovered", 0)):
+        m, idx, cnt = _one_row(g["s"], g["overlap"], cov, g["alpha"], g["top_k"], g["past_chunks"])
+        assert list(m) == [_num(x) for x in g[case]["m"]], (case, m)
+        assert list(idx) == g[case]["kv_idx"] and cnt == g["top_k"], (case, idx)
+
+
+def test_fp32_decision_example():
+    g = golden("ex6_fp32_decision.json")
+    C = g["past_chunks"]
+    s = np.asarray(g["s"], np.float32).reshape(1, 1, 1, -1)
+    ov = np.asarray(g["overlap"], np.float32).reshape(1, 1, C)
+    cov = np.ones((1, 1), np.uint8)
+    m64 = O.modulate(s.astype(np.float64), ov, cov, 1, 1, g["alpha"])
+    m32 = O.modulate(s, ov, cov, 1, 1, g["alpha"], fp32=True)
+    assert list(O.select(m64, g["top_k"])[0][0, 0, 0]) == g["fp64"]["kv_idx"]
+    assert list(m32[0, 0, 0]) == [_num(x) for x in g["fp32"]["m"]]
+    assert list(O.select(m32, g["top_k"])[0][0, 0, 0]) == g["fp32"]["kv_idx"]
+
+
+def test_zero_alpha_zero_overlap_uncovered_are_native():
+    rng = np.random.default_rng(1)
+    B, H, nq, C, blk, T = 2, 3, 4, 5, 2, 8
+    nk = (C + 1) * T // blk
+    s = rng.standard_normal((B, H, nq, nk))
+    ov = rng.random((B, nq, C)).astype(np.float32)
+    cur = np.arange(nk) * blk // T == C
+    native = np.where(cur, np.inf, s)
+    cov1 = np.ones((B, nq), np.uint8)
+    assert np.array_equal(O.modulate(s, ov, cov1, blk, T, 0.0), native)
+    assert np.array_equal(O.modulate(s, np.zeros_like(ov), cov1, blk, T, 3.0), native)
+    assert np.array_equal(O.modulate(s, ov, np.zeros((B, nq), np.uint8), blk, T, 3.0), native)
+    # covered rows do change where overlap is non-zero
+    assert not np.array_equal(O.modulate(s, ov, cov1, blk, T, 3.0), native)
+    # the per-(b, query block) overlap row is used: row i of batch b reads overlap[b, i, chunk(j)]
+    m = O.modulate(s, ov, cov1, blk, T, 2.0)
+    b, h, i, j = 1, 2, 3, 5
+    c = j * blk // T
+    assert m[b, h, i, j] == s[b, h, i, j] * (1.0 + 2.0 * float(ov[b, i, c]))
+
+
+def _brute_force_topk(m_row, k):
+    """The unique subset S of size k with: j in S, j' not in S => m_j > m_j' or (m_j == m_j' and j < j')."""
+    nk = len(m_row)
+    keff = min(k, nk)
+    found = []
+    for S in itertools.combinations(range(nk), keff):
+        Sset = set(S)
+        ok = all((m_row[a] > m_row[b]) or (m_row[a] == m_row[b] and a < b)
+                 for a in Sset for b in range(nk) if b not in Sset)
+        if ok:
+            found.append(S)
+    assert len(found) == 1
+    return list(found[0])
+
+
+def test_select_matches_brute_force_with_ties():
+    rng = np.random.default_rng(2)
+    vals = np.array([-1.0, -0.5, -0.0, 0.0, 0.5, 1.0, np.inf])
+    for trial in range(60):
+        nk = int(rng.integers(1, 10))
+        k = int(rng.integers(1, 12))
+        m = rng.choice(vals, size=nk)
+        idx, cnt, kth = O.select(m[None], k)
+        keff = min(k, nk)
+        expect = _brute_force_topk(list(m), k)
+        assert list(idx[0, :keff]) == expect and int(cnt[0]) == keff
+        assert np.all(idx[0, keff:] == -1)
+        assert kth[0] == min(m[j] for j in expect) or kth[0] == m[sorted(expect, key=lambda j: (-m[j], j))[-1]]
+
+
+def test_select_keep_all_and_current_only():
+    rng = np.random.default_rng(3)
+    B, H, nq, C, blk, T = 1, 2, 2, 4, 2, 4
+    nk, ncur = (C + 1) * T // blk, T // blk
+    s = rng.standard_normal((B, H, nq, nk))
+    m = O.modulate(s, rng.random((B, nq, C)).astype(np.float32), np.ones((B, nq), np.uint8), blk, T, 1.0)
+    idx, cnt, _ = O.select(m, nk + 3)
+    assert np.all(cnt == nk) and np.all(idx[..., :nk] == np.arange(nk)) and np.all(idx[..., nk:] == -1)
+    idx, cnt, kth = O.select(m, ncur)
+    assert np.all(idx == np.arange(nk - ncur, nk)) and np.all(np.isinf(kth))
+
+
+def test_raising_overlap_keeps_positive_blocks():
+    # for s_j > 0, raising the overlap of chunk(j) never removes j
+    rng = np.random.default_rng(4)
+    C, blk, T, k = 6, 1, 1, 4
+    nk = C + 1
+    for _ in range(200):
+        s = rng.standard_normal((1, 1, 1, nk))
+        ov = rng.random((1, 1, C)).astype(np.float32)
+        cov = np.ones((1, 1), np.uint8)
+        before = set(O.select(O.modulate(s, ov, cov, blk, T, 1.5), k)[0][0, 0, 0])
+        j = int(rng.integers(0, C))
+        if s[0, 0, 0, j] <= 0 or j not in before:
+            continue
+        ov2 = ov.copy()
+        ov2[0, 0, j] = min(1.0, ov2[0, 0, j] + 0.5)
+        after = set(O.select(O.modulate(s, ov2, cov, blk, T, 1.5), k)[0][0, 0, 0])
+        assert j in after
+
+
+# ---------------------------------------------------------------- attention
+
+def test_two_key_closed_form():
+    # blk = 1, d = 4: logits 0 and q.k1/2 = 1 -> out = (v0 + e v1)/(1 + e), lse = log(1 + e)
+    q = np.array([[[[2, 0, 0, 0]]]], np.float32)
+    k = np.array([[[[0, 0, 0, 0], [1, 0, 0, 0]]]], np.float32)
+    v = np.array([[[[1, 2, 3, 4], [-1, 0, 5, 8]]]], np.float32)
+    e = math.e
+    expect = (np.array([1, 2, 3, 4]) + e * np.array([-1, 0, 5, 8])) / (1 + e)
+    for out, lse in (O.dense_attn(q, k, v),
+                     O.attn(q, k, v, np.array([[[[0, 1]]]], np.int32), np.array([[[2]]], np.int32), 1)):
+        assert np.allclose(out[0, 0, 0], expect, rtol=0, atol=1e-14)
+        assert abs(lse[0, 0, 0] - math.log(1 + e)) < 1e-14
+
+
+def test_zero_query_mean_of_kept_values_and_poison():
+    g = golden("ex3_zero_query_mask.json")
+    blk, T, C, d = g["block"], g["chunk_tokens"], g["past_chunks"], g["head_dim"]
+    N = (C + 1) * T
+    q = np.zeros((1, 1, T, d), np.float32)
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    v = np.zeros((1, 1, N, d), np.float32)
+    for j, val in enumerate(g["v_fill_per_block"]):
+        v[0, 0, j * blk:(j + 1) * blk] = val
+    nq = T // blk
+    idx = np.array(g["kv_idx"], np.int32)[None, None, None].repeat(nq, axis=2)
+    cnt = np.full((1, 1, nq), len(g["kv_idx"]), np.int32)
+    out, lse = O.attn(q, k, v, idx, cnt, blk)
+    assert np.all(out == g["expected_out"])
+    assert np.allclose(lse, math.log(len(g["kv_idx"]) * blk), rtol=0, atol=1e-14)
+    # poison the skipped block with NaN: nothing changes
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, blk:2 * blk] = np.nan
+    v2[0, 0, blk:2 * blk] = np.nan
+    out2, lse2 = O.attn(q, k2, v2, idx, cnt, blk)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_keep_all_equals_dense_and_list_order_is_irrelevant():
+    cfg = get_config("tiny").with_(chunk_tokens=64, past_chunks=3, block=16, top_k=1000)
+    x = make_inputs(cfg)
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    assert np.all(r["kv_cnt"] == cfg.nk)
+    out, lse = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block)
+    dout, dlse = O.dense_attn(x.q, x.k, x.v)
+    assert np.max(np.abs(out - dout)) <= 1e-12 and np.max(np.abs(lse - dlse)) <= 1e-12
+    perm = r["kv_idx"][..., :cfg.nk][..., ::-1].copy()
+    pout, _ = O.attn(x.q, x.k, x.v, perm, r["kv_cnt"], cfg.block)
+    assert np.max(np.abs(pout - out)) <= 1e-12
+
+
+def test_single_block_zero_keys_gives_block_mean_of_values():
+    d, blk, T = 8, 4, 4
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, T, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 3 * T, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 3 * T, d)).astype(np.float32)
+    k[0, 0, 2 * blk:3 * blk] = 0.0
+    out, _ = O.attn(q, k, v, np.array([[[[2]]]], np.int32), np.array([[[1]]], np.int32), blk)
+    expect = v[0, 0, 2 * blk:3 * blk].astype(np.float64).sum(0) / blk
+    assert np.allclose(out[0, 0], expect[None, :], rtol=0, atol=1e-14)
+
+
+def test_current_only_attends_within_current_chunk():
+    cfg = get_config("tiny").with_(chunk_tokens=32, past_chunks=2, block=16, top_k=2)
+    x = make_inputs(cfg)
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    assert np.all(r["kv_idx"] == np.arange(cfg.nk - cfg.ncur, cfg.nk))
+    out, _ = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block)
+    T = cfg.chunk_tokens
+    dout, _ = O.dense_attn(x.q, x.k[:, :, -T:], x.v[:, :, -T:])
+    assert np.max(np.abs(out - dout)) <= 1e-12
+
+
+def test_bf16_inputs_are_widened_exactly():
+    # the oracle reads bf16 bit patterns exactly: same result as the widened float32 values
+    cfg = get_config("small").with_(heads=1, chunk_tokens=128, past_chunks=2, top_k=4)
+    x = make_inputs(cfg)
+    a = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    b = O.route(x.as_f32("q"), x.as_f32("k"), x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    assert np.array_equal(a["s"], b["s"]) and np.array_equal(a["kv_idx"], b["kv_idx"])
+
+
+# ---------------------------------------------------------------- the comparison rule itself
+
+def test_gap_rule_accepts_oracle_and_rejects_planted_errors():
+    cfg = get_config("small").with_(heads=2, chunk_tokens=256, past_chunks=6, top_k=10)
+    x = make_inputs(cfg)
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    cur_first = cfg.nk - cfg.ncur
+    st = check_selection(r["kv_idx"], r["kv_cnt"], r["m"], r["kth"], r["kv_idx"], cfg.k_eff, cur_first)
+    assert st["rows_differing"] == 0
+    # plant: replace the kept block with the lowest score by the best dropped block -> must fail
+    bad = r["kv_idx"].copy()
+    m0 = r["m"][0, 0, 0]
+    kept = [j for j in bad[0, 0, 0, :cfg.k_eff] if j < cur_first]
+    worst = min(kept, key=lambda j: m0[j])
+    dropped = [j for j in range(cur_first) if j not in set(bad[0, 0, 0])]
+    best = max(dropped, key=lambda j: m0[j])
+    if abs(m0[best] - r["kth"][0, 0, 0]) > 1e-4 or abs(m0[worst] - r["kth"][0, 0, 0]) > 1e-4:
+        row = sorted(set(bad[0, 0, 0, :cfg.k_eff]) - {worst} | {best})
+        bad[0, 0, 0, :cfg.k_eff] = row
+        with pytest.raises(AssertionError):
+            check_selection(bad, r["kv_cnt"], r["m"], r["kth"], r["kv_idx"], cfg.k_eff, cur_first)
+    # plant: drop a current block -> must fail
+    bad2 = r["kv_idx"].copy()
+    bad2[0, 0, 0, cfg.k_eff - 1] = bad2[0, 0, 0, 0] - 1 if bad2[0, 0, 0, 0] > 0 else 0
+    with pytest.raises(AssertionError):
+        check_selection(bad2, r["kv_cnt"], r["m"], r["kth"], r["kv_idx"], cfg.k_eff, cur_first)
