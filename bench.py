@@ -1,0 +1,226 @@
+"""Benchmark of one routed attention layer (velox_route + velox_sparse_attn) on one MI355X.
+
+A step is one full layer over one batch of synthetic input resident in HBM:
+pooled block scoring, overlap modulation + per-row top-k, and block-skipping
+attention, for every head of the workload.  Prints one JSON line:
+value = effective TFLOP/s (QK^T + PV FLOPs of the executed tiles / layer time);
+ms_per_step = ms per layer.  Also reports the dense-equivalent rate, per-kernel
+times, the roofline fraction of the attention kernel (HIP events on the launch
+stream), the routing phase's HBM fraction, and the CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
+    ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
+    return ap.parse_args()
+
+
+def file_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_src):
+    """HBM bytes per launch measured with rocprofv3 PMC counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_sparse_fa_headline.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != file_sha(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer runs on a single MI355X "
+              "(head sharding across GPUs is a design note, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import geometry_routed_block_velox_amd as velox
+    from synth import get_config, make_inputs
+
+    cfg = get_config(args.config)
+    t0 = time.time()
+    x = make_inputs(cfg)
+    print(f"[bench] inputs for {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+
+    def up(a, cast=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if cast and a.dtype == np.uint16:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.cuda()
+
+    q, k, v = up(x.q, bf), up(x.k, bf), up(x.v, bf)
+    ov, cov = up(x.overlap), up(x.covered)
+    B, H, nq = cfg.batch, cfg.heads, cfg.nq
+    kv_idx = torch.empty((B, H, nq, cfg.top_k), dtype=torch.int32, device="cuda")
+    kv_cnt = torch.empty((B, H, nq), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    p = velox.problem_for(tuple(q.shape), k.shape[2], cfg.block, cfg.top_k, cfg.alpha,
+                          velox.VELOX_BF16 if bf else velox.VELOX_F32)
+    ws = torch.empty(velox.velox_route_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        velox.route(q, k, ov, cov, cfg.block, cfg.top_k, cfg.alpha, out=(kv_idx, kv_cnt), workspace=ws)
+        if e is not None:
+            e[1].record(stream)
+        velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    route_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    attn_ms = [b.elapsed_time(c) for _, b, c in ev]
+    layer_ms = [a.elapsed_time(c) for a, _, c in ev]
+    ms_step = wall * 1e3 / args.steps
+
+    cnt = kv_cnt.cpu().numpy()
+    f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
+    f_dense = float(cfg.flops_dense())
+    gi = kv_idx.cpu().numpy()
+    union_blocks = sum(len(np.unique(gi[b, h][gi[b, h] >= 0])) for b in range(B) for h in range(H))
+    el = 2 if bf else 4
+    kv_block_bytes = 2 * cfg.block * cfg.head_dim * el
+    attn_bytes = 2 * q.numel() * el + union_blocks * kv_block_bytes
+    route_bytes = (q.numel() + k.numel()) * el + x.overlap.nbytes + x.covered.nbytes + gi.nbytes + cnt.nbytes
+    attn_avg = float(np.mean(attn_ms))
+    route_avg = float(np.mean(route_ms))
+    achieved = f_exec / (attn_avg * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "geometry_routed_block_velox_amd", "csrc", "sparse_fa.hip")
+    res = {
+        "metric": "ms/layer + effective TFLOP/s of routed sparse attention at chunk 48, 1 GPU",
+        "value": round(f_exec / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B{B} H{H} d{cfg.head_dim} T{cfg.chunk_tokens} chunk{cfg.past_chunks} "
+                        f"(N={cfg.kv_tokens}) blk{cfg.block} top-k{cfg.top_k} alpha{cfg.alpha}",
+            "global_batch": B, "seq_len": cfg.kv_tokens, "parallelism": "none (1 GPU)",
+        },
+        "ms_per_layer_events_median": round(float(np.median(layer_ms)), 4),
+        "route_ms": round(route_avg, 4),
+        "attn_ms": round(attn_avg, 4),
+        "dense_equiv_tflops": round(f_dense / (ms_step * 1e-3) / 1e12, 2),
+        "flops_exec": f_exec,
+        "flops_dense": f_dense,
+        "route_hbm": {"bytes": route_bytes, "achieved_GBs": round(route_bytes / (route_avg * 1e-3) / 1e9, 1),
+                      "peak_GBs": PEAK_HBM_GBS,
+                      "frac": round(route_bytes / (route_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {
+            "kernel": "velox_sparse_fa (sparse_fa_bf16_kernel)" if bf else "sparse_fa_f32_kernel",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles(kernel_src),
+            "algorithmic_bytes": attn_bytes,
+            "kv_union_blocks": union_blocks,
+        },
+    }
+
+    if not args.no_context:
+        # keep-all through the same kernel: the same-kernel "dense" comparison at this chunk
+        full_idx = torch.arange(cfg.nk, dtype=torch.int32, device="cuda").expand(B, H, nq, cfg.nk).contiguous()
+        full_cnt = torch.full((B, H, nq), cfg.nk, dtype=torch.int32, device="cuda")
+        velox.sparse_attn(q, k, v, full_idx, full_cnt, cfg.block, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 3
+        for _ in range(reps):
+            velox.sparse_attn(q, k, v, full_idx, full_cnt, cfg.block, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        keep_all_ms = e0.elapsed_time(e1) / reps
+        res["context_keep_all"] = {"attn_ms": round(keep_all_ms, 4),
+                                   "tflops": round(f_dense / (keep_all_ms * 1e-3) / 1e12, 2),
+                                   "attention_speedup_vs_keep_all": round(keep_all_ms / attn_avg, 3),
+                                   "layer_speedup_vs_keep_all": round(keep_all_ms / ms_step, 3)}
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, x, gi, cnt, n_tokens):
+    """The oracle (fp64, OpenMP) on this host: full routing plus attention for a
+    sample of query tokens, scaled to the whole layer."""
+    import platform
+
+    import numpy as np
+
+    from oracle import velox_oracle as O
+
+    t0 = time.perf_counter()
+    O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    t_route = time.perf_counter() - t0
+    total = cfg.batch * cfg.heads * cfg.chunk_tokens
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(total, size=min(n_tokens, total), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    O.attn(x.q, x.k, x.v, gi, cnt, cfg.block, tokens=toks)
+    t_attn = time.perf_counter() - t0
+    t_layer = t_route + t_attn * total / toks.size
+    f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(f_exec / t_layer / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle", "ms_per_layer": round(t_layer * 1e3, 1), "route_s": round(t_route, 3),
+            "attn_sample_s": round(t_attn, 3), "cpu_model": model,
+            "sample": f"full routing of all {cfg.rows} rows + fp64 attention of {toks.size} of {total} query "
+                      f"tokens (seeded uniform sample) on the same inputs and GPU block lists, attention time "
+                      f"scaled by {total / toks.size:.1f}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""Velox routed block-sparse attention for MI355X (gfx950): Python binding.
+
+Thin ctypes binding over the C ABI of libvelox.so (include/velox.h).  It only
+marshals arguments: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  There is
+no CPU fallback: if the library is missing or a call fails, an exception is
+raised.
+
+Entry points (same names as the C ABI):
+  velox_check(problem) -> status
+  velox_route_workspace_bytes(problem) -> int
+  route(q, k, overlap, covered, block, top_k, alpha, ...) -> (kv_idx, kv_cnt[, scores])
+  select(scores, overlap, covered, block, top_k, alpha) -> (kv_idx, kv_cnt)
+  sparse_attn(q, k, v, kv_idx, kv_cnt, block, ...) -> out[, lse]
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
+    "route", "select", "sparse_attn", "problem_for",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libvelox.so")
+
+VELOX_F32, VELOX_BF16 = 0, 1
+MAX_QUERY_BLOCKS, MAX_KV_BLOCKS = 64, 8192
+
+
+class Status:
+    OK, NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = range(7)
+
+
+class VeloxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().velox_status_string(status).decode()
+        if status == Status.HIP:
+            msg += f" (hipError_t {lib().velox_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+class Problem(C.Structure):
+    """Mirror of `velox_problem` in include/velox.h."""
+    _fields_ = [
+        ("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32), ("chunk_tokens", C.c_int32),
+        ("past_chunks", C.c_int32), ("block", C.c_int32), ("top_k", C.c_int32), ("alpha", C.c_float),
+        ("dtype", C.c_int32),
+    ]
+
+    @property
+    def nq(self):
+        return self.chunk_tokens // self.block
+
+    @property
+    def nk(self):
+        return (self.past_chunks + 1) * self.chunk_tokens // self.block
+
+    def __repr__(self):
+        return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def lib():
+    """Load libvelox.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it with geometry_routed_block_velox_amd/build.py "
+                              "(or __graft_entry__.build())")
+        L = C.CDLL(library_path)
+        P, V = C.POINTER(Problem), C.c_void_p
+        L.velox_check.argtypes = [P]
+        L.velox_check.restype = C.c_int
+        L.velox_route_workspace_bytes.argtypes = [P]
+        L.velox_route_workspace_bytes.restype = C.c_size_t
+        L.velox_route.argtypes = [P, V, V, V, V, V, V, V, V, C.c_size_t, V]
+        L.velox_route.restype = C.c_int
+        L.velox_select.argtypes = [P, V, V, V, V, V, V]
+        L.velox_select.restype = C.c_int
+        L.velox_sparse_attn.argtypes = [P, V, V, V, V, V, V, V, V]
+        L.velox_sparse_attn.restype = C.c_int
+        L.velox_status_string.argtypes = [C.c_int]
+        L.velox_status_string.restype = C.c_char_p
+        L.velox_last_hip_error.argtypes = []
+        L.velox_last_hip_error.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def velox_check(p: Problem) -> int:
+    return lib().velox_check(C.byref(p))
+
+
+def velox_route_workspace_bytes(p: Problem) -> int:
+    return lib().velox_route_workspace_bytes(C.byref(p))
+
+
+def _raise(status: int, where: str):
+    if status != Status.OK:
+        raise VeloxError(status, where)
+
+
+# ---------------------------------------------------------------- torch front end
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return VELOX_BF16
+    if t.dtype == torch.float32:
+        return VELOX_F32
+    raise TypeError(f"Q/K/V must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def problem_for(q_shape, kv_tokens: int, block: int, top_k: int, alpha: float, dtype: int) -> Problem:
+    """Build a Problem from Q's shape [B,H,T,d] and the KV length N = (C+1)*T."""
+    B, H, T, d = q_shape
+    if T <= 0 or kv_tokens % T:
+        raise ValueError(f"KV length {kv_tokens} is not a whole number of chunks of {T} tokens")
+    return Problem(B, H, d, T, kv_tokens // T - 1, block, top_k, float(alpha), dtype)
+
+
+def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_scores: bool = False,
+          out=None, workspace=None, stream=None):
+    """velox_route: returns (kv_idx [B,H,nq,top_k] int32, kv_cnt [B,H,nq] int32[, scores fp32])."""
+    torch = _torch()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, ndim=4)
+    p = problem_for(tuple(q.shape), k.shape[2], block, top_k, alpha, _dtype_code(q))
+    _raise(velox_check(p), "velox_route")
+    B, H, T, d = q.shape
+    if tuple(k.shape) != (B, H, k.shape[2], d):
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    C_ = p.past_chunks
+    if C_ > 0:
+        _dev(overlap, "overlap", torch.float32)
+        if tuple(overlap.shape) != (B, p.nq, C_):
+            raise ValueError(f"overlap must be [{B},{p.nq},{C_}], got {tuple(overlap.shape)}")
+    else:
+        overlap = None
+    _dev(covered, "covered", torch.uint8)
+    if tuple(covered.shape) != (B, p.nq):
+        raise ValueError(f"covered must be [{B},{p.nq}], got {tuple(covered.shape)}")
+    if out is None:
+        kv_idx = torch.empty((B, H, p.nq, top_k), dtype=torch.int32, device=q.device)
+        kv_cnt = torch.empty((B, H, p.nq), dtype=torch.int32, device=q.device)
+    else:
+        kv_idx, kv_cnt = out
+    scores = torch.empty((B, H, p.nq, p.nk), dtype=torch.float32, device=q.device) if return_scores else None
+    need = velox_route_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().velox_route(C.byref(p), _ptr(q), _ptr(k), _ptr(overlap), _ptr(covered), _ptr(kv_idx), _ptr(kv_cnt),
+                           _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
+    _raise(st, "velox_route")
+    return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
+
+
+def select(scores, overlap, covered, block: int, top_k: int, alpha: float, stream=None):
+    """velox_select: modulation + top-k from given scores [B,H,nq,nk] (float32)."""
+    torch = _torch()
+    _dev(scores, "scores", torch.float32, ndim=4)
+    B, H, nq, nk = scores.shape
+    if nk % nq:
+        raise ValueError("nk must be a whole number of chunks of nq blocks")
+    p = Problem(B, H, 64, nq * block, nk // nq - 1, block, top_k, float(alpha), VELOX_F32)
+    _raise(velox_check(p), "velox_select")
+    if p.past_chunks > 0:
+        _dev(overlap, "overlap", torch.float32)
+        if tuple(overlap.shape) != (B, nq, p.past_chunks):
+            raise ValueError("overlap shape mismatch")
+    else:
+        overlap = None
+    _dev(covered, "covered", torch.uint8)
+    if tuple(covered.shape) != (B, nq):
+        raise ValueError("covered shape mismatch")
+    kv_idx = torch.empty((B, H, nq, top_k), dtype=torch.int32, device=scores.device)
+    kv_cnt = torch.empty((B, H, nq), dtype=torch.int32, device=scores.device)
+    st = lib().velox_select(C.byref(p), _ptr(scores), _ptr(overlap), _ptr(covered), _ptr(kv_idx), _ptr(kv_cnt),
+                            _stream(stream))
+    _raise(st, "velox_select")
+    return kv_idx, kv_cnt
+
+
+def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, out=None, stream=None):
+    """velox_sparse_attn: returns out [B,H,T,d] (dtype of q)[, lse [B,H,T] float32]."""
+    torch = _torch()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, ndim=4)
+    _dev(v, "v", q.dtype, ndim=4)
+    _dev(kv_idx, "kv_idx", torch.int32, ndim=4)
+    _dev(kv_cnt, "kv_cnt", torch.int32, ndim=3)
+    B, H, T, d = q.shape
+    p = problem_for(tuple(q.shape), k.shape[2], block, kv_idx.shape[3], 0.0, _dtype_code(q))
+    if tuple(k.shape) != tuple(v.shape) or tuple(k.shape[:2]) != (B, H) or k.shape[3] != d:
+        raise ValueError("k/v shape mismatch")
+    if tuple(kv_idx.shape[:3]) != (B, H, p.nq) or tuple(kv_cnt.shape) != (B, H, p.nq):
+        raise ValueError("kv_idx/kv_cnt shape mismatch")
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib().velox_sparse_attn(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
+                                 _ptr(lse), _stream(stream))
+    _raise(st, "velox_sparse_attn")
+    return (o, lse) if return_lse else o

@@ -1,0 +1,179 @@
+// velox_block_score: mean-pooled block importance.
+//
+// The article (sns.style "Velox", Deep analysis) modulates the block
+// importance the model already computes in every layer; here that
+// importance is the dot product of the mean-pooled query block and the
+// mean-pooled key block, scaled by 1/sqrt(d):
+//   qbar_i = mean of Q over query block i, kbar_j = mean of K over KV block j,
+//   s[b,h,i,j] = <qbar_i, kbar_j> / sqrt(d).
+//
+// Two launches:
+//   pool_queries_kernel  Q [B,H,T,d] -> qbar [B,H,nq,d] (float32 workspace).
+//   block_score_kernel   streams K once: each workgroup pools JB consecutive
+//                        KV blocks of one (b,h) and scores them against the
+//                        head's qbar kept in LDS.
+// Both are HBM-bound streaming reads (about 0.25 FLOP per byte).  Each wave
+// pools a whole block with 16-byte loads: a wave-wide load covers 64*16 B of
+// consecutive rows, the per-lane partial sums are folded with lane
+// exchanges, so a block needs no barrier.  Sums are float32.
+#include "velox_internal.h"
+
+namespace velox {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Bf16In {
+  using T = uint16_t;
+  static constexpr int VEC = 8;  // elements per 16-byte load
+  static __device__ __forceinline__ void add(const u32x4& r, float* acc) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+struct F32In {
+  using T = float;
+  static constexpr int VEC = 4;
+  static __device__ __forceinline__ void add(const u32x4& r, float* acc) {
+    acc[0] += __uint_as_float(r.x);
+    acc[1] += __uint_as_float(r.y);
+    acc[2] += __uint_as_float(r.z);
+    acc[3] += __uint_as_float(r.w);
+  }
+};
+
+// One wave pools a [BLK, D] block at `src` into D floats at `dst`
+// (written by the first CPR lanes).  Lane l reads 16-byte chunk l % CPR of
+// rows l / CPR + RPI * it, so every wave-wide load is one contiguous 1 KiB
+// span of the block.
+template <class E, int D, int BLK>
+__device__ __forceinline__ void wave_pool(const typename E::T* __restrict__ src, float* __restrict__ dst,
+                                          int lane) {
+  constexpr int VEC = E::VEC;
+  constexpr int CPR = D / VEC;   // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per wave-wide load
+  constexpr int NIT = BLK / RPI;
+  static_assert(CPR <= 64 && 64 % CPR == 0 && BLK % RPI == 0, "bad pooling shape");
+  const int c = lane % CPR;
+  const u32x4* p = reinterpret_cast<const u32x4*>(src) + (lane / CPR) * CPR + c;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  // Loads are issued in batches of up to 16 (64 VGPRs) before they are consumed.
+  constexpr int NB = NIT < 16 ? NIT : 16;
+  static_assert(NIT % NB == 0, "bad batch");
+#pragma unroll
+  for (int b0 = 0; b0 < NIT; b0 += NB) {
+    u32x4 r[NB];
+#pragma unroll
+    for (int it = 0; it < NB; ++it) r[it] = __builtin_nontemporal_load(p + (b0 + it) * RPI * CPR);
+#pragma unroll
+    for (int it = 0; it < NB; ++it) E::add(r[it], acc);
+  }
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
+  if (lane < CPR) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) dst[c * VEC + v] = acc[v] * (1.0f / BLK);
+  }
+}
+
+// One wave per query block: grid = ceil(B*H*nq / 4) workgroups of 256.
+template <class E, int D, int BLK>
+__global__ __launch_bounds__(256) void pool_queries_kernel(const typename E::T* __restrict__ q,
+                                                           float* __restrict__ qbar, int nblocks) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + wave;
+  if (g >= nblocks) return;
+  wave_pool<E, D, BLK>(q + (size_t)g * BLK * D, qbar + (size_t)g * D, lane);
+}
+
+constexpr int kJB = 16;  // KV blocks per scoring workgroup
+
+// grid = (ceil(nk / JB), B*H); 256 threads; dynamic LDS (nq + JB) * (D + 1) floats.
+template <class E, int D, int BLK>
+__global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* __restrict__ k,
+                                                          const float* __restrict__ qbar,
+                                                          float* __restrict__ scores, int nq, int nk) {
+  extern __shared__ float lds[];
+  constexpr int LD = D + 1;  // padded row: consecutive rows fall in different banks
+  float* qs = lds;
+  float* ks = lds + nq * LD;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.y;
+  const int j0 = blockIdx.x * kJB;
+  const int jn = min(kJB, nk - j0);
+
+  const float* qh = qbar + (size_t)bh * nq * D;
+  for (int x = tid; x < nq * D; x += 256) qs[(x / D) * LD + x % D] = qh[x];
+
+  const typename E::T* kh = k + (size_t)bh * nk * BLK * D;
+  for (int jj = wave; jj < jn; jj += 4) wave_pool<E, D, BLK>(kh + (size_t)(j0 + jj) * BLK * D, ks + jj * LD, lane);
+  __syncthreads();
+
+  const float rs = 1.0f / sqrtf((float)D);
+  float* sh = scores + (size_t)bh * nq * nk;
+  for (int pi = tid; pi < nq * kJB; pi += 256) {
+    const int i = pi / kJB, jj = pi % kJB;
+    if (jj < jn) {
+      const float* a = qs + i * LD;
+      const float* b = ks + jj * LD;
+      float dot = 0.f;
+#pragma unroll 16
+      for (int e = 0; e < D; ++e) dot += a[e] * b[e];
+      sh[(size_t)i * nk + j0 + jj] = dot * rs;
+    }
+  }
+}
+
+template <class E, int D, int BLK>
+hipError_t pool_q(const Dims& x, const void* q, float* qbar, hipStream_t s) {
+  const int nblocks = x.B * x.H * x.nq;
+  hipLaunchKernelGGL((pool_queries_kernel<E, D, BLK>), dim3((nblocks + 3) / 4), dim3(256), 0, s,
+                     static_cast<const typename E::T*>(q), qbar, nblocks);
+  return hipGetLastError();
+}
+
+template <class E, int D, int BLK>
+hipError_t score(const Dims& x, const void* k, const float* qbar, float* scores, hipStream_t s) {
+  const size_t lds = (size_t)(x.nq + kJB) * (D + 1) * sizeof(float);
+  hipLaunchKernelGGL((block_score_kernel<E, D, BLK>), dim3((x.nk + kJB - 1) / kJB, x.B * x.H), dim3(256), lds, s,
+                     static_cast<const typename E::T*>(k), qbar, scores, x.nq, x.nk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define VELOX_DISPATCH(FN, ...)                                                         \
+  do {                                                                                  \
+    const bool bf = p.dtype == VELOX_BF16;                                              \
+    if (p.head_dim == 128 && p.block == 128)                                            \
+      return bf ? FN<Bf16In, 128, 128>(__VA_ARGS__) : FN<F32In, 128, 128>(__VA_ARGS__); \
+    if (p.head_dim == 128 && p.block == 64)                                             \
+      return bf ? FN<Bf16In, 128, 64>(__VA_ARGS__) : FN<F32In, 128, 64>(__VA_ARGS__);   \
+    if (p.head_dim == 64 && p.block == 128)                                             \
+      return bf ? FN<Bf16In, 64, 128>(__VA_ARGS__) : FN<F32In, 64, 128>(__VA_ARGS__);   \
+    if (p.head_dim == 64 && p.block == 64)                                              \
+      return bf ? FN<Bf16In, 64, 64>(__VA_ARGS__) : FN<F32In, 64, 64>(__VA_ARGS__);     \
+    return hipErrorInvalidValue;                                                        \
+  } while (0)
+
+hipError_t launch_pool_queries(const velox_problem& p, const void* q, float* qbar, hipStream_t s) {
+  const Dims x = dims(p);
+  VELOX_DISPATCH(pool_q, x, q, qbar, s);
+}
+
+hipError_t launch_block_score(const velox_problem& p, const void* k, const float* qbar, float* scores,
+                              hipStream_t s) {
+  const Dims x = dims(p);
+  VELOX_DISPATCH(score, x, k, qbar, scores, s);
+}
+
+}  // namespace velox

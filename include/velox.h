@@ -1,0 +1,156 @@
+/*
+ * velox.h -- C ABI of the Velox routed block-sparse attention layer for
+ * AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * The method (sns.style, "Velox: spatial memory speeds up video world
+ * models", section Deep analysis, all four language editions): a chunked
+ * video-diffusion model keeps a KV cache that grows by one chunk per step.
+ * In every attention layer Velox takes the block importance the model
+ * already computes, softly modulates it by how much each past chunk's
+ * camera-frustum slice overlaps the query region, leaves regions that the
+ * history does not cover on the model's native routing, keeps the most
+ * important KV blocks per query block, and runs tiled attention that
+ * skips the other blocks.  Routing decisions are made at the kernel's tile
+ * size so that skipped blocks are really skipped (same section, paragraph
+ * on token-block granularity).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *    owned by the caller.  Q, K, V and Out must be 16-byte aligned.
+ *  - The library never allocates, frees, synchronises or prints.  Calls
+ *    enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ *    and return immediately.
+ *  - Arguments are validated on the host before any launch; on an error
+ *    nothing is launched and nothing is written.
+ *  - Device data is trusted apart from block lists: NaN or Inf in Q, K,
+ *    V, scores or overlap give unspecified (but memory-safe) results.
+ *  - Functions are thread-safe; the library holds no state except the
+ *    thread-local HIP error code of the last failed launch.
+ *
+ * Shapes (notation of the problem struct below):
+ *   nq = T / blk query blocks, nk = N / blk KV blocks with N = (C+1)*T,
+ *   ncur = T / blk current-chunk blocks (the last ncur KV blocks),
+ *   chunk(j) = floor(j*blk / T) is the chunk of KV block j (C = current),
+ *   k_eff = min(top_k, nk); a "row" is one (b, h, i) query block.
+ */
+#ifndef VELOX_H_
+#define VELOX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *velox_stream_t;
+
+typedef enum velox_status {
+  VELOX_OK = 0,
+  VELOX_ERR_NULL_POINTER = 1, /* a required pointer is NULL                                  */
+  VELOX_ERR_BAD_SHAPE = 2,    /* sizes < 1, T % blk != 0, top_k < ncur, alpha < 0 or not finite */
+  VELOX_ERR_UNSUPPORTED = 3,  /* (dtype, d, blk) not built, or nq / nk above the limits below */
+  VELOX_ERR_MISALIGNED = 4,   /* Q, K, V or Out not 16-byte aligned                          */
+  VELOX_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than velox_route_workspace_bytes  */
+  VELOX_ERR_HIP = 6           /* a launch failed; velox_last_hip_error() holds the hipError_t */
+} velox_status;
+
+typedef enum velox_dtype { VELOX_F32 = 0, VELOX_BF16 = 1 } velox_dtype;
+
+/* Built configurations: d in {64, 128}, blk in {64, 128}, both dtypes.
+ * Limits: nq <= VELOX_MAX_QUERY_BLOCKS, nk <= VELOX_MAX_KV_BLOCKS. */
+#define VELOX_MAX_QUERY_BLOCKS 64
+#define VELOX_MAX_KV_BLOCKS 8192
+
+typedef struct velox_problem {
+  int32_t batch;        /* B: independent rollouts                                         */
+  int32_t heads;        /* H: heads, equal for Q and KV                                    */
+  int32_t head_dim;     /* d                                                               */
+  int32_t chunk_tokens; /* T: query tokens = tokens per chunk                              */
+  int32_t past_chunks;  /* C >= 0: number of past chunks; N = (C+1)*T KV tokens, the
+                           current chunk being the last T of them                          */
+  int32_t block;        /* blk: routing block = attention tile, for queries and keys       */
+  int32_t top_k;        /* kept KV blocks per row including the ncur current blocks
+                           (top_k >= ncur); values above nk keep every block               */
+  float alpha;          /* modulation strength, finite and >= 0                            */
+  velox_dtype dtype;    /* element type of Q, K, V and Out                                 */
+} velox_problem;
+
+/* Validate a problem on the host (no GPU needed).  Returns VELOX_OK,
+ * VELOX_ERR_NULL_POINTER (p == NULL), VELOX_ERR_BAD_SHAPE or
+ * VELOX_ERR_UNSUPPORTED. */
+velox_status velox_check(const velox_problem *p);
+
+/* Bytes of device workspace velox_route needs for this problem (pooled
+ * queries and, when `scores` is NULL, the score matrix); 0 if p is invalid. */
+size_t velox_route_workspace_bytes(const velox_problem *p);
+
+/* Routing: block importance, overlap modulation and per-row top-k
+ * (sns.style "Velox" article, Deep analysis, third and fourth steps).
+ *
+ *   q        [B,H,T,d]  dtype         queries of the current chunk
+ *   k        [B,H,N,d]  dtype         keys of the whole cache (past chunks, then current)
+ *   overlap  [B,nq,C]   float32       frustum-slice overlap of query block i with past
+ *                                     chunk c, expected in [0,1] (not clamped); may be
+ *                                     NULL when C == 0
+ *   covered  [B,nq]     uint8         0 = history does not cover the region: native
+ *                                     routing (no modulation); non-zero = covered
+ *   kv_idx   [B,H,nq,top_k] int32 out kept KV block ids of each row, ascending; the
+ *                                     entries after the first k_eff are -1
+ *   kv_cnt   [B,H,nq]   int32   out   k_eff for every row
+ *   scores   [B,H,nq,nk] float32 out  optional: the raw importance s (NULL = not written)
+ *   workspace, workspace_bytes        device scratch of at least
+ *                                     velox_route_workspace_bytes(p) bytes, 256-byte aligned
+ *
+ * Per row (b,h,i): qbar_i and kbar_j are the means of Q over query block i
+ * and of K over KV block j (float32 sums); s_j = <qbar_i, kbar_j>/sqrt(d);
+ * m_j = +inf for current-chunk blocks, s_j*(1 + alpha*overlap[b,i,chunk(j)])
+ * for past blocks of covered rows, s_j otherwise (every operation a
+ * separately rounded float32 operation).  The kept set is the k_eff largest
+ * m_j, ties broken toward the lower block index (-0 equals +0). */
+velox_status velox_route(const velox_problem *p, const void *q, const void *k, const float *overlap,
+                         const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, float *scores,
+                         void *workspace, size_t workspace_bytes, velox_stream_t stream);
+
+/* The modulation and top-k steps of velox_route alone, from importance
+ * scores the caller provides (`scores` [B,H,nq,nk] float32, device; read
+ * only).  Same outputs and rules as velox_route; q and k are not needed. */
+velox_status velox_select(const velox_problem *p, const float *scores, const float *overlap,
+                          const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, velox_stream_t stream);
+
+/* Block-skipping tiled attention (sns.style "Velox" article, Deep analysis,
+ * paragraph on token-block granularity and FlashAttention-style tiles).
+ * p->top_k is the row stride of kv_idx (any value >= 1; the routing bound
+ * top_k >= ncur does not apply here) and p->alpha is ignored but must be
+ * valid.
+ *
+ *   q [B,H,T,d], k and v [B,H,N,d]      dtype
+ *   kv_idx [B,H,nq,top_k] int32, kv_cnt [B,H,nq] int32: per row the KV blocks
+ *        to attend; the first min(max(kv_cnt,0), top_k) entries are used and
+ *        entries outside [0, nk) are skipped, so a bad list never reads out
+ *        of bounds.  Lists need not be sorted; a block listed twice counts twice.
+ *   out [B,H,T,d] dtype out: for query token t of block i,
+ *        softmax(q_t K_U^T / sqrt(d)) V_U over the tokens U of the listed
+ *        blocks (no causal mask); bf16 output is rounded to nearest even.
+ *        A row with no valid block gets zeros.
+ *   lse [B,H,T] float32 out, optional (NULL = not written): natural-log
+ *        sum of exp of the scaled logits (-inf for an empty row).
+ * Arithmetic: bf16 MFMA products with float32 accumulation, float32 softmax;
+ * the probabilities are rounded to bf16 before the PV product.  float32
+ * problems use float32 throughout. */
+velox_status velox_sparse_attn(const velox_problem *p, const void *q, const void *k, const void *v,
+                               const int32_t *kv_idx, const int32_t *kv_cnt, void *out, float *lse,
+                               velox_stream_t stream);
+
+/* Static English description of a status code. */
+const char *velox_status_string(velox_status s);
+
+/* hipError_t of the last failed launch on the calling thread (0 = none). */
+int velox_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VELOX_H_ */

@@ -1,0 +1,106 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol, and
+validates arguments on the host before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import geometry_routed_block_velox_amd as velox
+from geometry_routed_block_velox_amd import Problem, Status
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "velox.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(velox_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
+            "velox_status_string", "velox_last_hip_error"} <= set(names)
+    lib = C.CDLL(velox.library_path)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def headline():
+    return Problem(1, 24, 128, 4096, 48, 128, 256, 2.0, velox.VELOX_BF16)
+
+
+def test_check_accepts_every_workload():
+    from synth import CONFIGS
+    for cfg in CONFIGS.values():
+        p = Problem(cfg.batch, cfg.heads, cfg.head_dim, cfg.chunk_tokens, cfg.past_chunks, cfg.block, cfg.top_k,
+                    cfg.alpha, velox.VELOX_BF16 if cfg.dtype == "bf16" else velox.VELOX_F32)
+        assert velox.velox_check(p) == Status.OK, cfg.name
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, Status.BAD_SHAPE), ("heads", 0, Status.BAD_SHAPE), ("past_chunks", -1, Status.BAD_SHAPE),
+    ("chunk_tokens", 4000, Status.BAD_SHAPE), ("chunk_tokens", 64, Status.BAD_SHAPE),
+    ("top_k", 31, Status.BAD_SHAPE), ("alpha", -1.0, Status.BAD_SHAPE), ("alpha", float("nan"), Status.BAD_SHAPE),
+    ("alpha", float("inf"), Status.BAD_SHAPE), ("head_dim", 96, Status.UNSUPPORTED),
+    ("block", 32, Status.UNSUPPORTED), ("dtype", 7, Status.UNSUPPORTED),
+    ("chunk_tokens", 128 * 65, Status.UNSUPPORTED), ("past_chunks", 300, Status.UNSUPPORTED),
+])
+def test_check_rejects(field, value, status):
+    p = headline()
+    setattr(p, field, value)
+    assert velox.velox_check(p) == status
+    assert velox.velox_route_workspace_bytes(p) == 0
+
+
+def test_check_null_and_limits():
+    assert velox.lib().velox_check(None) == Status.NULL_POINTER
+    p = headline()
+    p.top_k = 10_000  # above nk: keep-all, still valid
+    assert velox.velox_check(p) == Status.OK
+    p = headline()
+    p.past_chunks = 255  # nk = 256*32 = 8192, the limit
+    assert velox.velox_check(p) == Status.OK
+
+
+def test_workspace_bytes():
+    p = headline()
+    rows = 24 * 32
+    expect = rows * 128 * 4 + ((rows * 1568 * 4 + 255) // 256) * 256
+    assert velox.velox_route_workspace_bytes(p) == expect
+
+
+def test_entry_points_validate_before_launch():
+    # Every call below fails host-side validation, so nothing touches a GPU.
+    L = velox.lib()
+    p = headline()
+    fake = C.c_void_p(0x100000)
+    mis = C.c_void_p(0x100001)
+    ws_need = velox.velox_route_workspace_bytes(p)
+    assert L.velox_route(C.byref(p), None, fake, fake, fake, fake, fake, None, fake, ws_need, None) == Status.NULL_POINTER
+    assert L.velox_route(C.byref(p), fake, fake, None, fake, fake, fake, None, fake, ws_need, None) == Status.NULL_POINTER
+    assert L.velox_route(C.byref(p), mis, fake, fake, fake, fake, fake, None, fake, ws_need, None) == Status.MISALIGNED
+    assert L.velox_route(C.byref(p), fake, fake, fake, fake, fake, fake, None, fake, ws_need - 1, None) == Status.WORKSPACE
+    assert L.velox_route(C.byref(p), fake, fake, fake, fake, fake, fake, None, None, ws_need, None) == Status.NULL_POINTER
+    assert L.velox_route(C.byref(p), fake, fake, fake, fake, fake, fake, None, C.c_void_p(0x100010), ws_need,
+                         None) == Status.WORKSPACE
+    bad = headline()
+    bad.top_k = 3
+    assert L.velox_route(C.byref(bad), fake, fake, fake, fake, fake, fake, None, fake, ws_need, None) == Status.BAD_SHAPE
+    assert L.velox_select(C.byref(p), None, fake, fake, fake, fake, None) == Status.NULL_POINTER
+    assert L.velox_sparse_attn(C.byref(p), fake, fake, mis, fake, fake, fake, None, None) == Status.MISALIGNED
+    assert L.velox_sparse_attn(C.byref(p), fake, fake, fake, None, fake, fake, None, None) == Status.NULL_POINTER
+    # attention accepts a list stride below ncur (user lists), routing does not
+    short = headline()
+    short.top_k = 4
+    assert L.velox_sparse_attn(C.byref(short), fake, fake, fake, None, fake, fake, None, None) == Status.NULL_POINTER
+    assert velox.velox_check(short) == Status.BAD_SHAPE
+    assert L.velox_last_hip_error() == 0
+
+
+def test_status_strings():
+    L = velox.lib()
+    for s in range(7):
+        assert L.velox_status_string(s)
+    assert L.velox_status_string(99) == b"unknown status"

@@ -1,0 +1,129 @@
+"""GPU path vs the CPU oracle on the five workloads (called through the C ABI).
+
+* Scores: the GPU's float32 pooled importance against the fp64 oracle.
+* Selection: the gap rule (membership must match wherever the oracle's
+  modulated score is more than 1e-4 from the row's k-th score; lists must be
+  valid everywhere).
+* Selection decision alone, in float32 on both sides: bit-exact.
+* Attention: GPU kernel and oracle fed the same (oracle) block lists,
+  max-abs 2e-2 / mean-abs 2e-3 for bf16, 1e-4 / 1e-5 for float32.
+Full sizes compare sampled rows and tokens; small sizes compare everything.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import geometry_routed_block_velox_amd as velox
+from oracle import velox_oracle as O
+from synth import get_config, make_inputs
+from tests.gpu_helpers import cached_inputs, dev_inputs, out_to_f64, sample_tokens, say, to_dev
+from tests.parity_rules import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, check_close,
+                                check_selection)
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny", "small", "mid", "headline", "stress"]
+SCORE_ATOL, SCORE_RTOL = 2e-5, 1e-5
+
+
+def tol(cfg):
+    return (BF16_MAX_ABS, BF16_MEAN_ABS) if cfg.dtype == "bf16" else (F32_MAX_ABS, F32_MEAN_ABS)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    velox.lib()
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_route_matches_oracle(name):
+    x = cached_inputs(name)
+    cfg = x.cfg
+    d = dev_inputs(x)
+    say(f"{name}: velox_route")
+    kv_idx, kv_cnt, scores = velox.route(d["q"], d["k"], d["overlap"], d["covered"], cfg.block, cfg.top_k,
+                                         cfg.alpha, return_scores=True)
+    torch.cuda.synchronize()
+    say(f"{name}: oracle route")
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    s_gpu = scores.cpu().numpy().astype(np.float64)
+    err = np.abs(s_gpu - r["s"])
+    bound = SCORE_ATOL + SCORE_RTOL * np.abs(r["s"])
+    say(f"{name}: score max err {err.max():.3g}, max err/bound {np.max(err / bound):.3g}")
+    assert np.all(err <= bound), f"scores: max err {err.max():.3g}"
+    st = check_selection(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), r["m"], r["kth"], r["kv_idx"], cfg.k_eff,
+                         cfg.nk - cfg.ncur)
+    say(f"{name}: selection {st}")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_select_decision_is_bit_exact(name):
+    """Same float32 scores on both sides, decision in float32: identical lists."""
+    cfg = get_config(name)
+    rng = np.random.default_rng(11)
+    B, H, nq, nk = cfg.batch, cfg.heads, cfg.nq, cfg.nk
+    s = rng.standard_normal((B, H, nq, nk)).astype(np.float32)
+    # plant exact ties, signed zeros and repeated values
+    s[..., ::7] = 0.25
+    s[..., 3::11] = -0.0
+    s[..., 5::11] = 0.0
+    s[..., 1::13] = np.round(s[..., 1::13], 1)
+    x = cached_inputs(name) if name in ("tiny", "small") else None
+    ov = x.overlap if x is not None else rng.random((B, nq, cfg.past_chunks)).astype(np.float32)
+    cov = x.covered if x is not None else (rng.random((B, nq)) > 0.3).astype(np.uint8)
+    say(f"{name}: velox_select")
+    kv_idx, kv_cnt = velox.select(to_dev(s), to_dev(ov), to_dev(cov), cfg.block, cfg.top_k, cfg.alpha)
+    m = O.modulate(s, ov, cov, cfg.block, cfg.chunk_tokens, cfg.alpha, fp32=True)
+    ref_idx, ref_cnt, _ = O.select(m, cfg.top_k)
+    assert np.array_equal(kv_idx.cpu().numpy(), ref_idx)
+    assert np.array_equal(kv_cnt.cpu().numpy(), ref_cnt)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_attention_matches_oracle_same_lists(name):
+    x = cached_inputs(name)
+    cfg = x.cfg
+    d = dev_inputs(x)
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    say(f"{name}: velox_sparse_attn on oracle lists")
+    out, lse = velox.sparse_attn(d["q"], d["k"], d["v"], to_dev(r["kv_idx"]), to_dev(r["kv_cnt"]), cfg.block,
+                                 return_lse=True)
+    torch.cuda.synchronize()
+    out = out_to_f64(out).reshape(-1, cfg.head_dim)
+    lse = lse.cpu().numpy().astype(np.float64).reshape(-1)
+    if cfg.rows <= 64:
+        toks = np.arange(cfg.batch * cfg.heads * cfg.chunk_tokens)
+    else:
+        toks, _ = sample_tokens(cfg, n_rows=24, per_row=6)
+    say(f"{name}: oracle attention on {toks.size} tokens")
+    ref, ref_lse = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block, tokens=toks)
+    mx, mn = check_close(out[toks], ref, *tol(cfg))
+    lmx, _ = check_close(lse[toks], ref_lse, 1e-3 if cfg.dtype == "bf16" else 1e-4, 1e-3, "lse")
+    say(f"{name}: out max {mx:.3g} mean {mn:.3g}; lse max {lmx:.3g}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "mid", "headline"])
+def test_end_to_end_layer(name):
+    """velox_route then velox_sparse_attn on the GPU; rows whose GPU list equals the
+    oracle's must match the oracle's attention, the rest pass the gap rule."""
+    x = cached_inputs(name)
+    cfg = x.cfg
+    d = dev_inputs(x)
+    kv_idx, kv_cnt = velox.route(d["q"], d["k"], d["overlap"], d["covered"], cfg.block, cfg.top_k, cfg.alpha)
+    out = velox.sparse_attn(d["q"], d["k"], d["v"], kv_idx, kv_cnt, cfg.block)
+    torch.cuda.synchronize()
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    gi = kv_idx.cpu().numpy()
+    check_selection(gi, kv_cnt.cpu().numpy(), r["m"], r["kth"], r["kv_idx"], cfg.k_eff, cfg.nk - cfg.ncur)
+    same_row = np.all(gi.reshape(cfg.rows, -1) == r["kv_idx"].reshape(cfg.rows, -1), axis=1)
+    if cfg.rows <= 64:
+        toks = np.arange(cfg.batch * cfg.heads * cfg.chunk_tokens)
+    else:
+        toks, _ = sample_tokens(cfg, n_rows=16, per_row=4, seed=1)
+    toks = toks[same_row[toks // cfg.block]]
+    say(f"{name}: end-to-end on {toks.size} tokens ({(~same_row).sum()} rows with in-band swaps)")
+    ref, _ = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block, tokens=toks)
+    check_close(out_to_f64(out).reshape(-1, cfg.head_dim)[toks], ref, *tol(cfg))
