@@ -8,25 +8,32 @@
 // computed with an online softmax over the list, one KV block (= one tile)
 // at a time.  No causal mask.
 //
-// bf16 kernel (sparse_fa_bf16_kernel), one workgroup per row, BLK/32 waves,
-// each wave owning 32 query tokens:
+// bf16 kernel (sparse_fa_bf16_kernel): one workgroup of 4 waves per row.
+//  * Work split: wave w owns query half w&1 and key half w>>1 of every tile
+//    (64 queries x 64 keys at blk = 128), so each K/V operand fragment read
+//    from LDS feeds two MFMAs.  The two key halves keep independent online
+//    softmax states that are merged once at the end of the row.
 //  * Scores are formed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: the accumulator then holds one query per lane
-//    (lane l: query l%32; keys 8(r/4) + 4(l/32) + r%4 of each 32-key tile),
-//    so softmax statistics need one cross-lane exchange (lane l <-> l^32) and
-//    the output rescale is a per-lane scalar.
-//  * O^T = V^T P^T takes P straight from the score registers as the B operand:
-//    the contraction over keys may use any key order as long as both operands
-//    agree, so the V^T tile is stored in LDS with the keys of every 16-key
-//    group permuted to match the accumulator's order; each A operand is then
-//    one 16-byte LDS read.  V^T is produced at staging time with an 8x8
-//    bf16 register transpose per thread.
-//  * K and V^T tiles are double-buffered in LDS (2 x 64 KiB at d = blk = 128):
-//    the global loads of the next listed block are issued before the MFMA
-//    work on the current one and written to the other buffer after it, one
-//    barrier per block.  16-byte LDS chunks are XOR-swizzled by row so that
-//    both the staging writes and the MFMA operand reads are conflict-free.
-//  * exp2 with log2(e)/sqrt(d) folded into one FMA; the hardware v_exp_f32.
+//    v_mfma_f32_32x32x16_bf16: lane l of an accumulator holds query l%32 and
+//    keys 8(r/4) + 4(l/32) + r%4, so softmax statistics need one lane
+//    exchange (l <-> l^32) and output rescaling is a per-lane scalar.
+//  * O^T += V^T P^T takes P from the score registers as the B operand.  The
+//    contraction may visit keys in any order as long as both operands agree;
+//    the V^T operand is read from the row-major V tile with the LDS
+//    transpose read ds_read_b64_tr_b16, whose 16-lane groups return lane i
+//    four consecutive rows of column i -- exactly the accumulator's key order.
+//  * K and V tiles go from HBM straight to LDS (global_load_lds_dwordx4, no
+//    register staging), double-buffered in two distinct LDS arrays so that
+//    the loads of the next listed block overlap the MFMA work on the current
+//    one; one barrier per block.  16-byte chunks are XOR-swizzled per row so
+//    that the MFMA operand reads of K and the transpose reads of V spread
+//    over the banks.
+//  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
+//    The running maximum is raised only when a wave's block maximum exceeds
+//    it by more than 8 in log2 units; until then probabilities may reach
+//    2^8, which float32 sums and bf16 P hold as well as values below 1, and
+//    the final normalisation uses the same maximum, so the result is the
+//    same softmax.
 //  * Workgroups are remapped so that the rows of one head run on one XCD and
 //    share its L2 while they walk their ascending block lists.
 // float32 kernel (sparse_fa_f32_kernel): one thread per query token, plain
@@ -38,8 +45,32 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+template <int D, int BLK>
+struct Fa {
+  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int QW = BLK / 2;            // queries per wave
+  static constexpr int KW = BLK / 2;            // keys per wave and tile
+  static constexpr int QT = QW / 32;            // 32-query MFMA tiles per wave
+  static constexpr int KTW = KW / 32;           // 32-key MFMA tiles per wave
+  static constexpr int DS = D / 16;             // MFMA k-steps over d (scores)
+  static constexpr int DT = D / 32;             // 32-row d tiles of O^T
+  static constexpr int PS = KW / 16;            // MFMA k-steps over keys (PV)
+  static constexpr int NCH = D / 8;             // 16-byte chunks per row
+  static constexpr int TILE_CHUNKS = BLK * NCH; // per K (or V) tile
+  static constexpr int SEGS_PER_WAVE = TILE_CHUNKS / 64 / NW;  // 1 KiB DMA segments
+  static_assert(QT >= 1 && KTW >= 1 && NCH >= 8 && SEGS_PER_WAVE >= 1, "unsupported tile shape");
+  static __device__ __forceinline__ int swz_k(int row) { return row & (NCH - 1); }
+  static __device__ __forceinline__ int swz_v(int row) { return (4 * row) & (NCH - 1); }
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   bf16x8 r;
@@ -55,230 +86,282 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-// Transpose an 8x8 block of bf16: in[r] holds row r (8 elements), out[e]
-// receives column e (element e of every row, in row order).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint4& a = in[2 * p];
-      const uint4& b = in[2 * p + 1];
-      const uint32_t aw = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
-      const uint32_t bw = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
-      w[p] = (e & 1) ? ((aw >> 16) | (bw & 0xFFFF0000u)) : ((aw & 0xFFFFu) | (bw << 16));
-    }
-    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
+// Issue the HBM -> LDS copies of KV block j (K into st[0, TILE), V into
+// st[TILE, 2*TILE)).  Lane l of DMA segment g writes 16-byte slot 64g + l,
+// i.e. row (64g + l) / NCH and physical chunk (64g + l) % NCH; it fetches the
+// logical chunk stored there under the row's swizzle.  Per-lane byte offsets
+// within the block are precomputed once per thread in DmaOffsets.
 template <int D, int BLK>
-struct FaShape {
-  static constexpr int NW = BLK / 32;              // waves, 32 queries each
-  static constexpr int NT = NW * 64;               // threads
-  static constexpr int KCH = D / 8;                // 16-byte chunks per K row
-  static constexpr int VCH = BLK / 8;              // 16-byte chunks per V^T row
-  static constexpr int TILE_CHUNKS = BLK * D / 8;  // 16-byte chunks per K (or V) tile
-  static constexpr int STAGE_CHUNKS = 2 * TILE_CHUNKS;
-  static constexpr int K_LOADS = TILE_CHUNKS / NT;            // K chunks per thread
-  static constexpr int V_ITEMS = (BLK / 16) * 2 * (D / 8);     // 8x8 transposes per tile
-  static constexpr int V_LOADS = (V_ITEMS + NT - 1) / NT;      // per thread
-  static constexpr size_t LDS_BYTES = 2 * STAGE_CHUNKS * 16;
-  static_assert(TILE_CHUNKS % NT == 0, "K tile must split evenly");
-  static_assert(KCH >= 8 && VCH >= 8, "swizzle needs 8 chunks per row");
+struct DmaOffsets {
+  using F = Fa<D, BLK>;
+  uint32_t k[F::SEGS_PER_WAVE];
+  uint32_t v[F::SEGS_PER_WAVE];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < F::SEGS_PER_WAVE; ++i) {
+      const int slot = (wave * F::SEGS_PER_WAVE + i) * 64 + lane;
+      const int row = slot / F::NCH, pc = slot % F::NCH;
+      k[i] = (uint32_t)(row * D + (pc ^ F::swz_k(row)) * 8) * 2u;
+      v[i] = (uint32_t)(row * D + (pc ^ F::swz_v(row)) * 8) * 2u;
+    }
+  }
 };
 
-// Global loads of one KV block into registers.
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l
+// fetches gbase + voff and the data lands at LDS byte lds + 16*l.  Written as
+// inline asm so that the compiler's wait-count pass does not treat every
+// later LDS read as a possible consumer of the copy; the kernel waits for
+// the copies itself (s_waitcnt vmcnt(0)) before the barrier that publishes
+// the tile.  The instruction writes no VGPR.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(gbase)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
 template <int D, int BLK>
-struct TileRegs {
-  using S = FaShape<D, BLK>;
-  uint4 k[S::K_LOADS];
-  uint4 v[S::V_LOADS][8];
+__device__ __forceinline__ void issue_tile(uint4* st, const uint16_t* __restrict__ kh,
+                                           const uint16_t* __restrict__ vh, int j, int wave,
+                                           const DmaOffsets<D, BLK>& off) {
+  using F = Fa<D, BLK>;
+  const uint16_t* kb = kh + (size_t)j * BLK * D;
+  const uint16_t* vb = vh + (size_t)j * BLK * D;
+  const uint32_t base = lds_addr(st);
+#pragma unroll
+  for (int i = 0; i < F::SEGS_PER_WAVE; ++i) {
+    const uint32_t seg = (uint32_t)(wave * F::SEGS_PER_WAVE + i);
+    lds_dma16(base + seg * 1024u, kb, off.k[i]);
+    lds_dma16(base + F::TILE_CHUNKS * 16u + seg * 1024u, vb, off.v[i]);
+  }
+}
+
+// Per-wave state of the online softmax over this wave's key half.
+template <int D, int BLK>
+struct WaveState {
+  using F = Fa<D, BLK>;
+  bf16x8 qf[F::QT][F::DS];     // Q fragments: B operand of S^T = K Q^T
+  f32x16 oacc[F::DT][F::QT];   // O^T accumulators
+  float m[F::QT];              // running maximum (raw logits) of query qc of tile qt
+  float l[F::QT];              // this lane's partial sum of probabilities
 };
 
+// One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, from the LDS stage st.
 template <int D, int BLK>
-__device__ __forceinline__ void load_tile(TileRegs<D, BLK>& r, const uint16_t* __restrict__ kh,
-                                          const uint16_t* __restrict__ vh, int j, int tid) {
-  using S = FaShape<D, BLK>;
-  const uint4* kb = reinterpret_cast<const uint4*>(kh + (size_t)j * BLK * D);
-  const uint4* vb = reinterpret_cast<const uint4*>(vh + (size_t)j * BLK * D);
+__device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* st, int kbase, int qc, int hh,
+                                             int lane, float scale_log2) {
+  using F = Fa<D, BLK>;
+  f32x16 sacc[F::KTW][F::QT];
 #pragma unroll
-  for (int m = 0; m < S::K_LOADS; ++m) r.k[m] = kb[tid + m * S::NT];
+  for (int kt = 0; kt < F::KTW; ++kt)
 #pragma unroll
-  for (int m = 0; m < S::V_LOADS; ++m) {
-    const int it = tid + m * S::NT;
-    if (S::V_ITEMS % S::NT == 0 || it < S::V_ITEMS) {
-      const int c = it % S::KCH, hh = (it / S::KCH) & 1, g = it / (2 * S::KCH);
+    for (int qt = 0; qt < F::QT; ++qt)
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int key = 16 * g + 4 * hh + (rr & 3) + ((rr >> 2) << 3);
-        r.v[m][rr] = vb[key * S::KCH + c];
+      for (int r = 0; r < 16; ++r) sacc[kt][qt][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < F::DS; ++s) {
+#pragma unroll
+    for (int kt = 0; kt < F::KTW; ++kt) {
+      const int row = kbase + 32 * kt + qc;
+      const bf16x8 a = as_bf16x8(st[row * F::NCH + ((2 * s + hh) ^ F::swz_k(row))]);
+#pragma unroll
+      for (int qt = 0; qt < F::QT; ++qt)
+        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
+    }
+  }
+
+  float mb[F::QT];
+#pragma unroll
+  for (int qt = 0; qt < F::QT; ++qt) {
+    float mx = sacc[0][qt][0];
+#pragma unroll
+    for (int kt = 0; kt < F::KTW; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool grow = (mx - w.m[qt]) * scale_log2 > kLazyRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(w.m[qt], mx);
+      const float resc = __builtin_amdgcn_exp2f((w.m[qt] - m_new) * scale_log2);
+      w.l[qt] *= resc;
+#pragma unroll
+      for (int dt = 0; dt < F::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] *= resc;
+      w.m[qt] = m_new;
+    }
+    mb[qt] = w.m[qt] * scale_log2;
+  }
+
+  // V^T operand for 16-key step ps and d tile dt: two transpose reads of keys
+  // kbase + 16ps + 8half + 4hh + 0..3, columns d = 32dt + 16gd + i.  The
+  // column swizzle depends only on the lane (key % 4 is fixed per lane).
+  const int grp = lane >> 4, j = lane & 15;
+  const int gd = grp & 1;
+  const int key0 = kbase + 4 * hh + (j >> 2);
+  const lds_u8_t* vbase = (const lds_u8_t*)(const lds_void_t*)st + F::TILE_CHUNKS * 16 + key0 * F::NCH * 16 +
+                          8 * (j & 1);
+  const int vsw = F::swz_v(key0);
+#pragma unroll
+  for (int ps = 0; ps < F::PS; ++ps) {
+    // P for these 16 keys: accumulator registers 8(ps%2)..+7 of key tile ps/2.
+    bf16x8 pb[F::QT];
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) {
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][qt][8 * (ps & 1) + i], scale_log2, -mb[qt]));
+        lsum += p;
+        pb[qt][i] = (__bf16)p;
       }
+      w.l[qt] += lsum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < F::DT; ++dt) {
+      const int c = (4 * dt + 2 * gd + ((j & 3) >> 1)) ^ vsw;
+      i16x4 part[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(vbase + (16 * ps + 8 * half) * F::NCH * 16 + c * 16));
+      bf16x8 a;
+      __builtin_memcpy(&a, part, 16);
+#pragma unroll
+      for (int qt = 0; qt < F::QT; ++qt)
+        w.oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt], w.oacc[dt][qt], 0, 0, 0);
     }
   }
 }
 
 template <int D, int BLK>
-__device__ __forceinline__ void store_tile(const TileRegs<D, BLK>& r, uint4* __restrict__ stage, int tid) {
-  using S = FaShape<D, BLK>;
-  uint4* ks = stage;
-  uint4* vs = stage + S::TILE_CHUNKS;
-#pragma unroll
-  for (int m = 0; m < S::K_LOADS; ++m) {
-    const int x = tid + m * S::NT;
-    const int row = x / S::KCH, c = x % S::KCH;
-    ks[row * S::KCH + (c ^ swz(row))] = r.k[m];
-  }
-#pragma unroll
-  for (int m = 0; m < S::V_LOADS; ++m) {
-    const int it = tid + m * S::NT;
-    if (S::V_ITEMS % S::NT == 0 || it < S::V_ITEMS) {
-      const int c = it % S::KCH, hh = (it / S::KCH) & 1, g = it / (2 * S::KCH);
-      uint4 t[8];
-      transpose8x8(r.v[m], t);
-      const int vc = 2 * g + hh;  // chunk of keys at positions 16g + 8hh .. +7
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * c + e;
-        vs[d * S::VCH + (vc ^ swz(d))] = t[e];
-      }
-    }
-  }
-}
-
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void sparse_fa_bf16_kernel(
+__global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2) {
-  using S = FaShape<D, BLK>;
-  constexpr int DS = D / 16;    // MFMA k-steps over d (scores)
-  constexpr int KT = BLK / 32;  // 32-key tiles per block
-  constexpr int DT = D / 32;    // 32-row d tiles of O^T
-  constexpr int PS = BLK / 16;  // MFMA k-steps over keys (PV)
-  extern __shared__ uint4 smem[];
+  using F = Fa<D, BLK>;
+  __shared__ uint4 bufA[2 * F::TILE_CHUNKS];
+  __shared__ uint4 bufB[2 * F::TILE_CHUNKS];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 1, kg = wave >> 1;
   const int qc = lane & 31, hh = lane >> 5;
+  const int kbase = kg * F::KW;
   const int row = xcd_grouped(blockIdx.x, gridDim.x);
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
   const uint16_t* kh = k + (size_t)bh * N * D;
   const uint16_t* vh = v + (size_t)bh * N * D;
-  const int32_t* list = kv_idx + (size_t)row * top_k;
+  // The list is read-only here and wave-uniform: scalar loads via the constant address space.
+  const __attribute__((address_space(4))) int32_t* list =
+      (const __attribute__((address_space(4))) int32_t*)(kv_idx + (size_t)row * top_k);
   const int cnt = min(max(kv_cnt[row], 0), top_k);
 
-  // Q fragments (B operand of S^T = K Q^T): query qc of this wave, d = 16s + 8hh + 0..7.
-  const int tq = iq * BLK + wave * 32 + qc;
-  const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)bh * nq * BLK + tq) * D);
-  bf16x8 qf[DS];
+  WaveState<D, BLK> w;
+  const size_t qrow0 = (size_t)bh * nq * BLK + (size_t)iq * BLK + qg * F::QW;
 #pragma unroll
-  for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(qrow[2 * s + hh]);
+  for (int qt = 0; qt < F::QT; ++qt) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + (qrow0 + 32 * qt + qc) * D);
+#pragma unroll
+    for (int s = 0; s < F::DS; ++s) w.qf[qt][s] = as_bf16x8(qrow[2 * s + hh]);
+    w.m[qt] = -__builtin_inff();
+    w.l[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < F::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
+  }
 
-  f32x16 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -__builtin_inff(), l_run = 0.f;
+  DmaOffsets<D, BLK> dma;
+  dma.init(wave, lane);
 
   auto next_valid = [&](int t) {
     while (t < cnt && (unsigned)list[t] >= (unsigned)nk) ++t;
     return t;
   };
 
-  TileRegs<D, BLK> regs;
+  // Two-stage pipeline over the list, unrolled by two so that each stage
+  // names its own LDS array: the loads into one never wait on reads of the other.
   int t = next_valid(0);
-  if (t < cnt) {
-    load_tile<D, BLK>(regs, kh, vh, list[t], tid);
-    store_tile<D, BLK>(regs, smem, tid);
-  }
+  if (t < cnt) issue_tile<D, BLK>(bufA, kh, vh, list[t], wave, dma);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int buf = 0;
   while (t < cnt) {
-    const int tn = next_valid(t + 1);
-    if (tn < cnt) load_tile<D, BLK>(regs, kh, vh, list[tn], tid);
-
-    const uint4* ks = smem + buf * S::STAGE_CHUNKS;
-    const uint4* vs = ks + S::TILE_CHUNKS;
-
-    // S^T tile: rows = keys 32kt + ..., cols = this wave's 32 queries.
-    f32x16 sacc[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-      const int krow = 32 * kt + qc;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 a = as_bf16x8(ks[krow * S::KCH + ((2 * s + hh) ^ swz(krow))]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
-      }
-    }
-
-    // Online softmax for query qc (keys split between lanes l and l^32).
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float resc = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    const float mb = m_new * scale_log2;
-    float lsum = 0.f;
-    bf16x8 pb[PS];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], scale_log2, -mb));
-        lsum += p;
-        pb[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    }
-    l_run = l_run * resc + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= resc;
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + qc;
-#pragma unroll
-      for (int s = 0; s < PS; ++s) {
-        const bf16x8 a = as_bf16x8(vs[d * S::VCH + ((2 * s + hh) ^ swz(d))]);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], oacc[dt], 0, 0, 0);
-      }
-    }
-
-    if (tn < cnt) store_tile<D, BLK>(regs, smem + (buf ^ 1) * S::STAGE_CHUNKS, tid);
+    int tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<D, BLK>(bufB, kh, vh, list[tn], wave, dma);
+    compute_tile<D, BLK>(w, bufA, kbase, qc, hh, lane, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
+    t = tn;
+    if (t >= cnt) break;
+    tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<D, BLK>(bufA, kh, vh, list[tn], wave, dma);
+    compute_tile<D, BLK>(w, bufB, kbase, qc, hh, lane, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     t = tn;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  uint16_t* orow = out + ((size_t)bh * nq * BLK + tq) * D;
+  // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0 through LDS.
+  float* xo = reinterpret_cast<float*>(bufA);  // [qg][dt][qt][r][lane]
+  float* xm = reinterpret_cast<float*>(bufB);  // m: [qg][qt][lane], then l: [qg][qt][lane]
+  float lw[F::QT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int qt = 0; qt < F::QT; ++qt) lw[qt] = w.l[qt] + __shfl_xor(w.l[qt], 32);
+  if (kg == 1) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * dt + 8 * rq + 4 * hh;
-      uint2 w;
-      w.x = pack_bf16x2(oacc[dt][4 * rq] * inv, oacc[dt][4 * rq + 1] * inv);
-      w.y = pack_bf16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d0) = w;
+    for (int qt = 0; qt < F::QT; ++qt) {
+      xm[(qg * F::QT + qt) * 64 + lane] = w.m[qt];
+      xm[((2 + qg) * F::QT + qt) * 64 + lane] = lw[qt];
+#pragma unroll
+      for (int dt = 0; dt < F::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(((qg * F::DT + dt) * F::QT + qt) * 16 + r) * 64 + lane] = w.oacc[dt][qt][r];
     }
   }
-  if (lse && hh == 0) {
-    lse[(size_t)bh * nq * BLK + tq] =
-        l_tot > 0.f ? (m_run * scale_log2 + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+  __syncthreads();
+  if (kg == 0) {
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) {
+      const float m1 = xm[(qg * F::QT + qt) * 64 + lane];
+      const float l1 = xm[((2 + qg) * F::QT + qt) * 64 + lane];
+      const float m0 = w.m[qt];
+      const float mm = fmaxf(m0, m1);
+      const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * scale_log2);
+      const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * scale_log2);
+      const float lt = lw[qt] * a0 + l1 * a1;
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const size_t tq = qrow0 + 32 * qt + qc;
+      uint16_t* orow = out + tq * D;
+#pragma unroll
+      for (int dt = 0; dt < F::DT; ++dt) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            const float o1 = xo[(((qg * F::DT + dt) * F::QT + qt) * 16 + r) * 64 + lane];
+            o[e] = (w.oacc[dt][qt][r] * a0 + o1 * a1) * inv;
+          }
+          uint2 pk;
+          pk.x = pack_bf16x2(o[0], o[1]);
+          pk.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * hh) = pk;
+        }
+      }
+      if (lse && hh == 0)
+        lse[tq] = lt > 0.f ? (mm * scale_log2 + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+    }
   }
 }
 
@@ -348,17 +431,12 @@ __global__ __launch_bounds__(BLK) void sparse_fa_f32_kernel(const float* __restr
 template <int D, int BLK>
 hipError_t fa_bf16(const Dims& x, const void* q, const void* k, const void* v, const int32_t* kv_idx,
                    const int32_t* kv_cnt, void* out, float* lse, hipStream_t s) {
-  using S = FaShape<D, BLK>;
-  auto kern = sparse_fa_bf16_kernel<D, BLK>;
-  // Thread-safe one-time opt-in to more than 64 KiB of dynamic LDS.
-  static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)S::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
   const int rows = x.B * x.H * x.nq;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(kern, dim3(rows), dim3(S::NT), S::LDS_BYTES, s, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), kv_idx, kv_cnt,
-                     static_cast<uint16_t*>(out), lse, x.nq, x.nk, x.top_k, scale_log2);
+  hipLaunchKernelGGL((sparse_fa_bf16_kernel<D, BLK>), dim3(rows), dim3(Fa<D, BLK>::NT), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), kv_idx, kv_cnt, static_cast<uint16_t*>(out), lse, x.nq, x.nk,
+                     x.top_k, scale_log2);
   return hipGetLastError();
 }
 
@@ -367,6 +445,7 @@ hipError_t fa_f32(const Dims& x, const void* q, const void* k, const void* v, co
                   const int32_t* kv_cnt, void* out, float* lse, hipStream_t s) {
   auto kern = sparse_fa_f32_kernel<D, BLK>;
   const size_t lds = 2 * (size_t)BLK * D * sizeof(float);
+  // Thread-safe one-time opt-in to more than 64 KiB of dynamic LDS.
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
