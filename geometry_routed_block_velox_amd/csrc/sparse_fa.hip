@@ -23,17 +23,21 @@
 //    transpose read ds_read_b64_tr_b16, whose 16-lane groups return lane i
 //    four consecutive rows of column i -- exactly the accumulator's key order.
 //  * K and V tiles go from HBM straight to LDS (global_load_lds_dwordx4, no
-//    register staging), double-buffered in two distinct LDS arrays so that
-//    the loads of the next listed block overlap the MFMA work on the current
-//    one; one barrier per block.  16-byte chunks are XOR-swizzled per row so
+//    register staging), double-buffered so that the loads of the next listed
+//    block overlap the MFMA work on the current one; one barrier per block.  16-byte chunks are XOR-swizzled per row so
 //    that the MFMA operand reads of K and the transpose reads of V spread
 //    over the banks.
 //  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
-//    The running maximum is raised only when a wave's block maximum exceeds
-//    it by more than 8 in log2 units; until then probabilities may reach
-//    2^8, which float32 sums and bf16 P hold as well as values below 1, and
-//    the final normalisation uses the same maximum, so the result is the
-//    same softmax.
+//    Each wave fixes its softmax reference maximum m_ref per query from the
+//    first listed block (the exact maximum over that block, so the largest
+//    probability is >= 1 and nothing underflows) and never rescales O inside
+//    the loop: later probabilities exp2((s - m_ref) c) may exceed 1, which
+//    float32 sums and bf16 P (same exponent range as float32) hold with the
+//    same relative precision, and the final normalisation uses the same
+//    m_ref, so the result is the same softmax.  If any block's probability
+//    sum exceeds 2^40 (logits more than 40 log2-units above the first
+//    block's maximum), the workgroup reruns the row: a max-only sweep finds
+//    the true maximum, then a second pass uses it (all probabilities <= 1).
 //  * Workgroups are remapped so that the rows of one head run on one XCD and
 //    share its L2 while they walk their ascending block lists.
 // float32 kernel (sparse_fa_f32_kernel): one thread per query token, plain
@@ -51,7 +55,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-constexpr float kLazyRescaleLog2 = 8.0f;
+// Per-block probability sum above which a row is recomputed at its true maximum.
+constexpr float kOverflowGuard = 1099511627776.0f;  // 2^40
 
 template <int D, int BLK>
 struct Fa {
@@ -149,12 +154,18 @@ struct WaveState {
   using F = Fa<D, BLK>;
   bf16x8 qf[F::QT][F::DS];     // Q fragments: B operand of S^T = K Q^T
   f32x16 oacc[F::DT][F::QT];   // O^T accumulators
-  float m[F::QT];              // running maximum (raw logits) of query qc of tile qt
+  float m[F::QT];              // reference maximum (raw logits) of query qc of tile qt
   float l[F::QT];              // this lane's partial sum of probabilities
+  bool bad;                    // a probability sum crossed kOverflowGuard
 };
 
-// One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, from the LDS stage st.
-template <int D, int BLK>
+enum class Mode { First, Normal, MaxOnly };
+
+// One tile from the LDS stage st: S^T = K Q^T, then
+//   Mode::First   m_ref = maximum of this tile's logits, then as Normal;
+//   Mode::Normal  P = exp2((S - m_ref) c), l += rowsum(P), O^T += V^T P^T;
+//   Mode::MaxOnly m_ref = max(m_ref, maximum of this tile's logits) only.
+template <Mode MODE, int D, int BLK>
 __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* st, int kbase, int qc, int hh,
                                              int lane, float scale_log2) {
   using F = Fa<D, BLK>;
@@ -178,28 +189,23 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
     }
   }
 
+  if constexpr (MODE != Mode::Normal) {
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) {
+      float mx = sacc[0][qt][0];
+#pragma unroll
+      for (int kt = 0; kt < F::KTW; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      w.m[qt] = MODE == Mode::First ? mx : fmaxf(w.m[qt], mx);
+    }
+  }
+  if constexpr (MODE == Mode::MaxOnly) return;
+
   float mb[F::QT];
 #pragma unroll
-  for (int qt = 0; qt < F::QT; ++qt) {
-    float mx = sacc[0][qt][0];
-#pragma unroll
-    for (int kt = 0; kt < F::KTW; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = (mx - w.m[qt]) * scale_log2 > kLazyRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(w.m[qt], mx);
-      const float resc = __builtin_amdgcn_exp2f((w.m[qt] - m_new) * scale_log2);
-      w.l[qt] *= resc;
-#pragma unroll
-      for (int dt = 0; dt < F::DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] *= resc;
-      w.m[qt] = m_new;
-    }
-    mb[qt] = w.m[qt] * scale_log2;
-  }
+  for (int qt = 0; qt < F::QT; ++qt) mb[qt] = w.m[qt] * scale_log2;
 
   // V^T operand for 16-key step ps and d tile dt: two transpose reads of keys
   // kbase + 16ps + 8half + 4hh + 0..3, columns d = 32dt + 16gd + i.  The
@@ -210,20 +216,21 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
   const lds_u8_t* vbase = (const lds_u8_t*)(const lds_void_t*)st + F::TILE_CHUNKS * 16 + key0 * F::NCH * 16 +
                           8 * (j & 1);
   const int vsw = F::swz_v(key0);
+  float lsum[F::QT];
+#pragma unroll
+  for (int qt = 0; qt < F::QT; ++qt) lsum[qt] = 0.f;
 #pragma unroll
   for (int ps = 0; ps < F::PS; ++ps) {
     // P for these 16 keys: accumulator registers 8(ps%2)..+7 of key tile ps/2.
     bf16x8 pb[F::QT];
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) {
-      float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][qt][8 * (ps & 1) + i], scale_log2, -mb[qt]));
-        lsum += p;
+        lsum[qt] += p;
         pb[qt][i] = (__bf16)p;
       }
-      w.l[qt] += lsum;
     }
 #pragma unroll
     for (int dt = 0; dt < F::DT; ++dt) {
@@ -240,6 +247,50 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
         w.oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt], w.oacc[dt][qt], 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int qt = 0; qt < F::QT; ++qt) {
+    w.l[qt] += lsum[qt];
+    w.bad |= lsum[qt] > kOverflowGuard;
+  }
+}
+
+// One pass over the row's block list with the two-stage copy pipeline: the
+// copies of the next listed block go into one LDS stage while the MFMA work
+// reads the other; one barrier per block.  FIRST_MODE applies to the first
+// listed block, MODE to the rest.
+template <Mode FIRST_MODE, Mode MODE, int D, int BLK>
+__device__ __forceinline__ void run_pass(WaveState<D, BLK>& w, uint4 (*stages)[2 * Fa<D, BLK>::TILE_CHUNKS],
+                                         const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
+                                         const __attribute__((address_space(4))) int32_t* list, int cnt, int nk,
+                                         int wave, const DmaOffsets<D, BLK>& dma, int kbase, int qc, int hh, int lane,
+                                         float scale_log2) {
+  auto next_valid = [&](int t) {
+    while (t < cnt && (unsigned)list[t] >= (unsigned)nk) ++t;
+    return t;
+  };
+  int t = next_valid(0);
+  if (t < cnt) issue_tile<D, BLK>(stages[0], kh, vh, list[t], wave, dma);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int buf = 0;
+  if (FIRST_MODE != MODE && t < cnt) {  // peeled first block
+    const int tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<D, BLK>(stages[1], kh, vh, list[tn], wave, dma);
+    compute_tile<FIRST_MODE, D, BLK>(w, stages[0], kbase, qc, hh, lane, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    buf = 1;
+    t = tn;
+  }
+  while (t < cnt) {
+    const int tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<D, BLK>(stages[buf ^ 1], kh, vh, list[tn], wave, dma);
+    compute_tile<MODE, D, BLK>(w, stages[buf], kbase, qc, hh, lane, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    buf ^= 1;
+    t = tn;
+  }
 }
 
 template <int D, int BLK>
@@ -248,8 +299,7 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2) {
   using F = Fa<D, BLK>;
-  __shared__ uint4 bufA[2 * F::TILE_CHUNKS];
-  __shared__ uint4 bufB[2 * F::TILE_CHUNKS];
+  __shared__ uint4 stages[2][2 * F::TILE_CHUNKS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,37 +333,30 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
 
   DmaOffsets<D, BLK> dma;
   dma.init(wave, lane);
-
-  auto next_valid = [&](int t) {
-    while (t < cnt && (unsigned)list[t] >= (unsigned)nk) ++t;
-    return t;
-  };
-
-  // Two-stage pipeline over the list, unrolled by two so that each stage
-  // names its own LDS array: the loads into one never wait on reads of the other.
-  int t = next_valid(0);
-  if (t < cnt) issue_tile<D, BLK>(bufA, kh, vh, list[t], wave, dma);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  while (t < cnt) {
-    int tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<D, BLK>(bufB, kh, vh, list[tn], wave, dma);
-    compute_tile<D, BLK>(w, bufA, kbase, qc, hh, lane, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    t = tn;
-    if (t >= cnt) break;
-    tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<D, BLK>(bufA, kh, vh, list[tn], wave, dma);
-    compute_tile<D, BLK>(w, bufB, kbase, qc, hh, lane, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    t = tn;
+  w.bad = false;
+  run_pass<Mode::First, Mode::Normal, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
+                                              scale_log2);
+  if (__syncthreads_or(w.bad)) {
+    // Rare: some logit exceeded the first block's maximum by more than 40
+    // log2-units.  Find each query's true maximum, then redo the row at it.
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) {
+      w.m[qt] = -__builtin_inff();
+      w.l[qt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < F::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
+    }
+    run_pass<Mode::MaxOnly, Mode::MaxOnly, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
+                                                   scale_log2);
+    run_pass<Mode::Normal, Mode::Normal, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
+                                                 scale_log2);
   }
 
   // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0 through LDS.
-  float* xo = reinterpret_cast<float*>(bufA);  // [qg][dt][qt][r][lane]
-  float* xm = reinterpret_cast<float*>(bufB);  // m: [qg][qt][lane], then l: [qg][qt][lane]
+  float* xo = reinterpret_cast<float*>(stages[0]);  // [qg][dt][qt][r][lane]
+  float* xm = reinterpret_cast<float*>(stages[1]);  // m: [qg][qt][lane], then l: [qg][qt][lane]
   float lw[F::QT];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) lw[qt] = w.l[qt] + __shfl_xor(w.l[qt], 32);

@@ -191,3 +191,37 @@ def test_unsorted_and_repeated_lists():
     out = velox.sparse_attn(d["q"], d["k"], d["v"], to_dev(lists), to_dev(cnt), cfg.block)
     ref, _ = O.attn(x.q, x.k, x.v, lists, cnt, cfg.block)
     check_close(out_to_f64(out), ref, *tol(cfg))
+
+
+@pytest.mark.parametrize("case", ["dominant-block", "two-close-blocks", "float32-overflow"])
+def test_logits_far_above_first_block_recompute_row(case):
+    """Logits more than 40 log2-units above the first listed block's maximum make
+    the kernel redo the row at the true maximum; the result must still match."""
+    cfg = get_config("small").with_(heads=2, chunk_tokens=128, past_chunks=4)
+    x = make_inputs(cfg)
+    from synth import f32_to_bf16_bits
+    q = np.ones((1, cfg.heads, cfg.chunk_tokens, cfg.head_dim), np.float32)
+    k = x.as_f32("k").copy()
+    k[:, :, 0:cfg.block] *= 0.1                      # first listed block: logits near 0
+    blk = cfg.block
+    if case == "dominant-block":
+        k[:, :, 3 * blk:4 * blk] = 6.0               # logit 48 with q = 1, d = 64
+        lists = [0, 2, 3, 5]
+    elif case == "float32-overflow":
+        # logit 160: exp2((160 - ~0) * log2 e) overflows float32, so this passes
+        # only if the row is recomputed at its true maximum
+        k[:, :, 3 * blk:4 * blk] = 20.0
+        lists = [0, 1, 3, 6]
+    else:
+        k[:, :, 2 * blk:3 * blk] = 4.0               # logit 32
+        k[:, :, 5 * blk:6 * blk] = 3.875             # logit 31, both blocks matter
+        lists = [0, 2, 5, 7]
+    qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+    idx = np.broadcast_to(np.array(lists, np.int32), (1, cfg.heads, cfg.nq, len(lists))).copy()
+    cnt = np.full((1, cfg.heads, cfg.nq), len(lists), np.int32)
+    out, lse = velox.sparse_attn(to_dev(qb, True), to_dev(kb, True), to_dev(x.v, True), to_dev(idx), to_dev(cnt),
+                                 cfg.block, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attn(qb, kb, x.v, idx, cnt, cfg.block)
+    check_close(out_to_f64(out), ref, *tol(cfg))
+    check_close(lse.cpu().numpy().astype(np.float64), ref_lse, 1e-3, 1e-3, "lse")
