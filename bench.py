@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first (reference for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -86,6 +88,12 @@ def main():
                           velox.VELOX_BF16 if bf else velox.VELOX_F32)
     ws = torch.empty(velox.velox_route_workspace_bytes(p), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
