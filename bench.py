@@ -189,9 +189,50 @@ def main():
                                    "attention_speedup_vs_keep_all": round(keep_all_ms / attn_avg, 3),
                                    "layer_speedup_vs_keep_all": round(keep_all_ms / ms_step, 3)}
 
+    res["route_cached"] = bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el,
+                                             x.overlap.nbytes + x.covered.nbytes + gi.nbytes + cnt.nbytes)
+
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el, small_bytes, reps=20):
+    """Routing from the pooled-key cache: the past chunks' pooled keys are filled once
+    (not timed), then velox_route_cached reads Q and the cached rows instead of K."""
+    import torch
+    B, H, nq, d = cfg.batch, cfg.heads, cfg.nq, cfg.head_dim
+    past = cfg.past_chunks * nq
+    kbar = torch.empty((B, H, max(past, 1), d), dtype=torch.float32, device="cuda")
+    velox.pool_keys(k, cfg.chunk_tokens, cfg.block, 0, past, kbar=kbar)
+    idx2 = torch.empty_like(kv_idx)
+    cnt2 = torch.empty_like(kv_cnt)
+    call = lambda: velox.route_cached(q, kbar, cfg.past_chunks, ov, cov, cfg.block, cfg.top_k, cfg.alpha,
+                                      out=(idx2, cnt2), workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx2, kv_idx) and torch.equal(cnt2, kv_cnt))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = q.numel() * el + B * H * past * d * 4 + small_bytes
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # one-time cost per finished chunk: pooling its nq blocks into the cache
+    e0.record(stream)
+    for _ in range(reps):
+        velox.pool_keys(k, cfg.chunk_tokens, cfg.block, max(past - nq, 0), min(nq, past), kbar=kbar)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pool_ms = e0.elapsed_time(e1) / reps
+    return {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "identical_to_route": same,
+            "pool_one_chunk_ms": round(pool_ms, 4),
+            "note": "velox_route_cached with the past chunks' pooled keys cached; pool_one_chunk_ms is the "
+                    "once-per-chunk velox_pool_keys cost of appending a finished chunk"}
 
 
 def cpu_baseline(cfg, x, gi, cnt, n_tokens):

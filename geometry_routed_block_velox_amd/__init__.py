@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   velox_check(problem) -> status
   velox_route_workspace_bytes(problem) -> int
   route(q, k, overlap, covered, block, top_k, alpha, ...) -> (kv_idx, kv_cnt[, scores])
+  pool_keys(k, chunk_tokens, block, first_block, num_blocks, ...) -> kbar cache
+  route_cached(q, kbar, past_chunks, overlap, covered, block, top_k, alpha, ...) -> as route
   select(scores, overlap, covered, block, top_k, alpha) -> (kv_idx, kv_cnt)
   sparse_attn(q, k, v, kv_idx, kv_cnt, block, ...) -> out[, lse]
 """
@@ -21,7 +23,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
-    "route", "select", "sparse_attn", "problem_for",
+    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +84,10 @@ def lib():
         L.velox_route_workspace_bytes.restype = C.c_size_t
         L.velox_route.argtypes = [P, V, V, V, V, V, V, V, V, C.c_size_t, V]
         L.velox_route.restype = C.c_int
+        L.velox_pool_keys.argtypes = [P, V, V, C.c_int32, C.c_int32, C.c_int32, V]
+        L.velox_pool_keys.restype = C.c_int
+        L.velox_route_cached.argtypes = [P, V, V, C.c_int32, V, V, V, V, V, V, C.c_size_t, V]
+        L.velox_route_cached.restype = C.c_int
         L.velox_select.argtypes = [P, V, V, V, V, V, V]
         L.velox_select.restype = C.c_int
         L.velox_sparse_attn.argtypes = [P, V, V, V, V, V, V, V, V]
@@ -188,6 +194,62 @@ def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_s
     st = lib().velox_route(C.byref(p), _ptr(q), _ptr(k), _ptr(overlap), _ptr(covered), _ptr(kv_idx), _ptr(kv_cnt),
                            _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "velox_route")
+    return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
+
+
+def pool_keys(k, chunk_tokens: int, block: int, first_block: int, num_blocks: int, kbar=None,
+              cache_blocks: int | None = None, stream=None):
+    """velox_pool_keys: pool KV blocks [first_block, first_block+num_blocks) of k [B,H,N,d] into the
+    float32 cache kbar [B,H,cache_blocks,d] (allocated with cache_blocks = N/block rows if not given)."""
+    torch = _torch()
+    _dev(k, "k", ndim=4)
+    B, H, N, d = k.shape
+    p = problem_for((B, H, chunk_tokens, d), N, block, 1, 0.0, _dtype_code(k))
+    if kbar is None:
+        cache_blocks = p.nk if cache_blocks is None else cache_blocks
+        kbar = torch.empty((B, H, cache_blocks, d), dtype=torch.float32, device=k.device)
+    _dev(kbar, "kbar", torch.float32, ndim=4)
+    if tuple(kbar.shape[:2]) != (B, H) or kbar.shape[3] != d:
+        raise ValueError(f"kbar shape {tuple(kbar.shape)} does not match k {tuple(k.shape)}")
+    st = lib().velox_pool_keys(C.byref(p), _ptr(k), _ptr(kbar), kbar.shape[2], first_block, num_blocks,
+                               _stream(stream))
+    _raise(st, "velox_pool_keys")
+    return kbar
+
+
+def route_cached(q, kbar, past_chunks: int, overlap, covered, block: int, top_k: int, alpha: float,
+                 return_scores: bool = False, out=None, workspace=None, stream=None):
+    """velox_route_cached: route from pooled keys kbar [B,H,cache_blocks,d] (float32) instead of K."""
+    torch = _torch()
+    _dev(q, "q", ndim=4)
+    _dev(kbar, "kbar", torch.float32, ndim=4)
+    B, H, T, d = q.shape
+    p = problem_for(tuple(q.shape), (past_chunks + 1) * T, block, top_k, alpha, _dtype_code(q))
+    _raise(velox_check(p), "velox_route_cached")
+    if tuple(kbar.shape[:2]) != (B, H) or kbar.shape[3] != d:
+        raise ValueError(f"kbar shape {tuple(kbar.shape)} does not match q {tuple(q.shape)}")
+    if past_chunks > 0:
+        _dev(overlap, "overlap", torch.float32)
+        if tuple(overlap.shape) != (B, p.nq, past_chunks):
+            raise ValueError(f"overlap must be [{B},{p.nq},{past_chunks}], got {tuple(overlap.shape)}")
+    else:
+        overlap = None
+    _dev(covered, "covered", torch.uint8)
+    if tuple(covered.shape) != (B, p.nq):
+        raise ValueError(f"covered must be [{B},{p.nq}], got {tuple(covered.shape)}")
+    if out is None:
+        kv_idx = torch.empty((B, H, p.nq, top_k), dtype=torch.int32, device=q.device)
+        kv_cnt = torch.empty((B, H, p.nq), dtype=torch.int32, device=q.device)
+    else:
+        kv_idx, kv_cnt = out
+    scores = torch.empty((B, H, p.nq, p.nk), dtype=torch.float32, device=q.device) if return_scores else None
+    need = velox_route_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().velox_route_cached(C.byref(p), _ptr(q), _ptr(kbar), kbar.shape[2], _ptr(overlap), _ptr(covered),
+                                  _ptr(kv_idx), _ptr(kv_cnt), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _raise(st, "velox_route_cached")
     return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
 
 

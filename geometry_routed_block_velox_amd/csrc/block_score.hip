@@ -12,7 +12,14 @@
 //   block_score_kernel   streams K once: each workgroup pools JB consecutive
 //                        KV blocks of one (b,h) and scores them against the
 //                        head's qbar kept in LDS.
-// Both are HBM-bound streaming reads (about 0.25 FLOP per byte).  Each wave
+// Cached variant (the article's Outlook section asks how the method behaves
+// for rollouts far longer than 48 chunks; past chunks' keys do not change,
+// so their pooled keys can be kept per layer):
+//   pool_keys_kernel     K blocks [first, first+num) -> float32 cache kbar.
+//   cached_score_kernel  scores from cached kbar rows instead of K.
+// Both pool with the same wave_pool() and score with the same score_rows(),
+// so cached and direct routing give bit-identical scores.
+// All are HBM-bound streaming reads (about 0.25 FLOP per byte).  Each wave
 // pools a whole block with 16-byte loads: a wave-wide load covers 64*16 B of
 // consecutive rows, the per-lane partial sums are folded with lane
 // exchanges, so a block needs no barrier.  Sums are float32.
@@ -97,30 +104,24 @@ __global__ __launch_bounds__(256) void pool_queries_kernel(const typename E::T* 
 
 constexpr int kJB = 16;  // KV blocks per scoring workgroup
 
-// grid = (ceil(nk / JB), B*H); 256 threads; dynamic LDS (nq + JB) * (D + 1) floats.
+// One wave per cached block: grid = ceil(B*H*num / 4) workgroups of 256.
 template <class E, int D, int BLK>
-__global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* __restrict__ k,
-                                                          const float* __restrict__ qbar,
-                                                          float* __restrict__ scores, int nq, int nk) {
-  extern __shared__ float lds[];
-  constexpr int LD = D + 1;  // padded row: consecutive rows fall in different banks
-  float* qs = lds;
-  float* ks = lds + nq * LD;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.y;
-  const int j0 = blockIdx.x * kJB;
-  const int jn = min(kJB, nk - j0);
+__global__ __launch_bounds__(256) void pool_keys_kernel(const typename E::T* __restrict__ k, float* __restrict__ kbar,
+                                                        int nk, int cache_blocks, int first, int num, int nitems) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + wave;
+  if (g >= nitems) return;
+  const int bh = g / num, j = first + g % num;
+  wave_pool<E, D, BLK>(k + ((size_t)bh * nk + j) * BLK * D, kbar + ((size_t)bh * cache_blocks + j) * D, lane);
+}
 
-  const float* qh = qbar + (size_t)bh * nq * D;
-  for (int x = tid; x < nq * D; x += 256) qs[(x / D) * LD + x % D] = qh[x];
-
-  const typename E::T* kh = k + (size_t)bh * nk * BLK * D;
-  for (int jj = wave; jj < jn; jj += 4) wave_pool<E, D, BLK>(kh + (size_t)(j0 + jj) * BLK * D, ks + jj * LD, lane);
-  __syncthreads();
-
+// s[i, j0+jj] = <qs_i, ks_jj> / sqrt(d) for the jn blocks staged in LDS (rows of D+1 floats).
+template <int D>
+__device__ __forceinline__ void score_rows(const float* qs, const float* ks, int nq, int jn, int j0, int nk,
+                                           float* __restrict__ sh) {
+  constexpr int LD = D + 1;
   const float rs = 1.0f / sqrtf((float)D);
-  float* sh = scores + (size_t)bh * nq * nk;
-  for (int pi = tid; pi < nq * kJB; pi += 256) {
+  for (int pi = threadIdx.x; pi < nq * kJB; pi += 256) {
     const int i = pi / kJB, jj = pi % kJB;
     if (jj < jn) {
       const float* a = qs + i * LD;
@@ -131,6 +132,54 @@ __global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* _
       sh[(size_t)i * nk + j0 + jj] = dot * rs;
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_qbar(const float* __restrict__ qh, float* qs, int nq) {
+  constexpr int LD = D + 1;
+  for (int x = threadIdx.x; x < nq * D; x += 256) qs[(x / D) * LD + x % D] = qh[x];
+}
+
+// grid = (ceil(nk / JB), B*H); 256 threads; dynamic LDS (nq + JB) * (D + 1) floats.
+template <class E, int D, int BLK>
+__global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* __restrict__ k,
+                                                          const float* __restrict__ qbar,
+                                                          float* __restrict__ scores, int nq, int nk) {
+  extern __shared__ float lds[];
+  constexpr int LD = D + 1;  // padded row: consecutive rows fall in different banks
+  float* qs = lds;
+  float* ks = lds + nq * LD;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.y;
+  const int j0 = blockIdx.x * kJB;
+  const int jn = min(kJB, nk - j0);
+
+  stage_qbar<D>(qbar + (size_t)bh * nq * D, qs, nq);
+  const typename E::T* kh = k + (size_t)bh * nk * BLK * D;
+  for (int jj = wave; jj < jn; jj += 4) wave_pool<E, D, BLK>(kh + (size_t)(j0 + jj) * BLK * D, ks + jj * LD, lane);
+  __syncthreads();
+  score_rows<D>(qs, ks, nq, jn, j0, nk, scores + (size_t)bh * nq * nk);
+}
+
+// Scores of KV blocks [0, nscore) from cached pooled keys kbar [B*H, cache_blocks, D].
+// grid = (ceil(nscore / JB), B*H); 256 threads; dynamic LDS as block_score_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void cached_score_kernel(const float* __restrict__ kbar,
+                                                           const float* __restrict__ qbar,
+                                                           float* __restrict__ scores, int nq, int nk,
+                                                           int cache_blocks, int nscore) {
+  extern __shared__ float lds[];
+  constexpr int LD = D + 1;
+  float* qs = lds;
+  float* ks = lds + nq * LD;
+  const int bh = blockIdx.y;
+  const int j0 = blockIdx.x * kJB;
+  const int jn = min(kJB, nscore - j0);
+  stage_qbar<D>(qbar + (size_t)bh * nq * D, qs, nq);
+  const float* kc = kbar + ((size_t)bh * cache_blocks + j0) * D;
+  for (int x = threadIdx.x; x < jn * D; x += 256) ks[(x / D) * LD + x % D] = kc[x];
+  __syncthreads();
+  score_rows<D>(qs, ks, nq, jn, j0, nk, scores + (size_t)bh * nq * nk);
 }
 
 template <class E, int D, int BLK>
@@ -146,6 +195,14 @@ hipError_t score(const Dims& x, const void* k, const float* qbar, float* scores,
   const size_t lds = (size_t)(x.nq + kJB) * (D + 1) * sizeof(float);
   hipLaunchKernelGGL((block_score_kernel<E, D, BLK>), dim3((x.nk + kJB - 1) / kJB, x.B * x.H), dim3(256), lds, s,
                      static_cast<const typename E::T*>(k), qbar, scores, x.nq, x.nk);
+  return hipGetLastError();
+}
+
+template <class E, int D, int BLK>
+hipError_t pool_k(const Dims& x, const void* k, float* kbar, int cache_blocks, int first, int num, hipStream_t s) {
+  const int nitems = x.B * x.H * num;
+  hipLaunchKernelGGL((pool_keys_kernel<E, D, BLK>), dim3((nitems + 3) / 4), dim3(256), 0, s,
+                     static_cast<const typename E::T*>(k), kbar, x.nk, cache_blocks, first, num, nitems);
   return hipGetLastError();
 }
 
@@ -174,6 +231,28 @@ hipError_t launch_block_score(const velox_problem& p, const void* k, const float
                               hipStream_t s) {
   const Dims x = dims(p);
   VELOX_DISPATCH(score, x, k, qbar, scores, s);
+}
+
+hipError_t launch_pool_keys(const velox_problem& p, const void* k, float* kbar, int cache_blocks, int first,
+                            int num, hipStream_t s) {
+  const Dims x = dims(p);
+  VELOX_DISPATCH(pool_k, x, k, kbar, cache_blocks, first, num, s);
+}
+
+hipError_t launch_cached_score(const velox_problem& p, const float* kbar, int cache_blocks, const float* qbar,
+                               float* scores, int nscore, hipStream_t s) {
+  const Dims x = dims(p);
+  const size_t lds = (size_t)(x.nq + kJB) * (x.d + 1) * sizeof(float);
+  const dim3 grid((nscore + kJB - 1) / kJB, x.B * x.H);
+  if (x.d == 128)
+    hipLaunchKernelGGL(cached_score_kernel<128>, grid, dim3(256), lds, s, kbar, qbar, scores, x.nq, x.nk,
+                       cache_blocks, nscore);
+  else if (x.d == 64)
+    hipLaunchKernelGGL(cached_score_kernel<64>, grid, dim3(256), lds, s, kbar, qbar, scores, x.nq, x.nk,
+                       cache_blocks, nscore);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace velox

@@ -76,6 +76,48 @@ velox_status velox_route(const velox_problem* p, const void* q, const void* k, c
   return hip_status(e);
 }
 
+velox_status velox_pool_keys(const velox_problem* p, const void* k, float* kbar, int32_t cache_blocks,
+                             int32_t first_block, int32_t num_blocks, velox_stream_t stream) {
+  const velox_status st = check_problem(p, false);
+  if (st != VELOX_OK) return st;
+  if (!k || !kbar) return VELOX_ERR_NULL_POINTER;
+  if (!aligned16(k) || !aligned16(kbar)) return VELOX_ERR_MISALIGNED;
+  const velox::Dims x = velox::dims(*p);
+  if (first_block < 0 || num_blocks < 0 || (int64_t)first_block + num_blocks > x.nk ||
+      (int64_t)first_block + num_blocks > cache_blocks)
+    return VELOX_ERR_BAD_SHAPE;
+  if ((int64_t)x.B * x.H * num_blocks > INT32_MAX - 3) return VELOX_ERR_UNSUPPORTED;
+  if (num_blocks == 0) return VELOX_OK;
+  return hip_status(velox::launch_pool_keys(*p, k, kbar, cache_blocks, first_block, num_blocks,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+velox_status velox_route_cached(const velox_problem* p, const void* q, const float* kbar, int32_t cache_blocks,
+                                const float* overlap, const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt,
+                                float* scores, void* workspace, size_t workspace_bytes, velox_stream_t stream) {
+  const velox_status st = velox_check(p);
+  if (st != VELOX_OK) return st;
+  if (!q || !kbar || !covered || !kv_idx || !kv_cnt || !workspace || (p->past_chunks > 0 && !overlap))
+    return VELOX_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(kbar)) return VELOX_ERR_MISALIGNED;
+  const velox::Dims x = velox::dims(*p);
+  // Blocks whose pooled keys are read: the past ones, plus the current chunk's
+  // when raw scores are returned (their selection does not depend on them).
+  const int nscore = scores ? x.nk : x.C * x.nq;
+  if (cache_blocks < 0 || cache_blocks < nscore) return VELOX_ERR_BAD_SHAPE;
+  if (workspace_bytes < velox_route_workspace_bytes(p) || ((uintptr_t)workspace & 255u))
+    return VELOX_ERR_WORKSPACE;
+  const size_t rows = (size_t)x.B * x.H * x.nq;
+  float* qbar = static_cast<float*>(workspace);
+  float* s = scores ? scores : reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                        align256(rows * x.d * sizeof(float)));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = velox::launch_pool_queries(*p, q, qbar, hs);
+  if (e == hipSuccess && nscore > 0) e = velox::launch_cached_score(*p, kbar, cache_blocks, qbar, s, nscore, hs);
+  if (e == hipSuccess) e = velox::launch_modulate_select(*p, s, overlap, covered, kv_idx, kv_cnt, hs);
+  return hip_status(e);
+}
+
 velox_status velox_select(const velox_problem* p, const float* scores, const float* overlap,
                           const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, velox_stream_t stream) {
   const velox_status st = velox_check(p);

@@ -13,6 +13,10 @@ namespace velox {
 hipError_t launch_pool_queries(const velox_problem& p, const void* q, float* qbar, hipStream_t s);
 hipError_t launch_block_score(const velox_problem& p, const void* k, const float* qbar, float* scores,
                               hipStream_t s);
+hipError_t launch_pool_keys(const velox_problem& p, const void* k, float* kbar, int cache_blocks, int first,
+                            int num, hipStream_t s);
+hipError_t launch_cached_score(const velox_problem& p, const float* kbar, int cache_blocks, const float* qbar,
+                               float* scores, int nscore, hipStream_t s);
 hipError_t launch_modulate_select(const velox_problem& p, const float* scores, const float* overlap,
                                   const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
 hipError_t launch_sparse_attn(const velox_problem& p, const void* q, const void* k, const void* v,

@@ -113,6 +113,35 @@ velox_status velox_route(const velox_problem *p, const void *q, const void *k, c
                          const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, float *scores,
                          void *workspace, size_t workspace_bytes, velox_stream_t stream);
 
+/* Incremental pooled-key cache (the article's Outlook section: behaviour for
+ * rollouts far longer than 48 chunks; with the cache kept per layer, past
+ * chunks' keys, which do not change, are pooled once instead of on every
+ * routing call).
+ *
+ * velox_pool_keys writes the float32 means of K over KV blocks
+ * [first_block, first_block + num_blocks) of every (b,h) into the cache:
+ *   k     [B,H,N,d] dtype   keys (N = (C+1)*T from p; top_k and alpha of p are
+ *                           not used but must be valid, top_k >= 1)
+ *   kbar  [B,H,cache_blocks,d] float32 out, 16-byte aligned; only the rows of
+ *                           the pooled blocks are written
+ * Requires 0 <= first_block, 0 <= num_blocks, first_block + num_blocks <= nk
+ * and <= cache_blocks (else VELOX_ERR_BAD_SHAPE).  num_blocks == 0 is a no-op.
+ * The values are bit-identical to the pooled keys velox_route computes. */
+velox_status velox_pool_keys(const velox_problem *p, const void *k, float *kbar, int32_t cache_blocks,
+                             int32_t first_block, int32_t num_blocks, velox_stream_t stream);
+
+/* velox_route with the pooled keys read from a cache filled by
+ * velox_pool_keys instead of pooled from K.  Rows [0, C*nq) of kbar (the
+ * past chunks) must hold the pooled keys; rows [C*nq, nk) (the current
+ * chunk) are read only when `scores` is requested, since the current chunk is
+ * always kept.  cache_blocks is kbar's row stride in blocks and must cover
+ * the rows read (else VELOX_ERR_BAD_SHAPE).  Other arguments, the workspace
+ * size and the outputs are those of velox_route, and for the same pooled
+ * keys the outputs are bit-identical to it. */
+velox_status velox_route_cached(const velox_problem *p, const void *q, const float *kbar, int32_t cache_blocks,
+                                const float *overlap, const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt,
+                                float *scores, void *workspace, size_t workspace_bytes, velox_stream_t stream);
+
 /* The modulation and top-k steps of velox_route alone, from importance
  * scores the caller provides (`scores` [B,H,nq,nk] float32, device; read
  * only).  Same outputs and rules as velox_route; q and k are not needed. */

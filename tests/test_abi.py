@@ -21,7 +21,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
-            "velox_status_string", "velox_last_hip_error"} <= set(names)
+            "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached"} <= set(names)
     lib = C.CDLL(velox.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -96,6 +96,35 @@ def test_entry_points_validate_before_launch():
     short.top_k = 4
     assert L.velox_sparse_attn(C.byref(short), fake, fake, fake, None, fake, fake, None, None) == Status.NULL_POINTER
     assert velox.velox_check(short) == Status.BAD_SHAPE
+    assert L.velox_last_hip_error() == 0
+
+
+def test_cache_entry_points_validate_before_launch():
+    L = velox.lib()
+    p = headline()  # nq = 32, nk = 1568, C = 48
+    fake = C.c_void_p(0x100000)
+    mis = C.c_void_p(0x100008)
+    nk = 1568
+    assert L.velox_pool_keys(C.byref(p), None, fake, nk, 0, 1, None) == Status.NULL_POINTER
+    assert L.velox_pool_keys(C.byref(p), fake, mis, nk, 0, 1, None) == Status.MISALIGNED
+    assert L.velox_pool_keys(C.byref(p), fake, fake, nk, -1, 1, None) == Status.BAD_SHAPE
+    assert L.velox_pool_keys(C.byref(p), fake, fake, nk, 0, -1, None) == Status.BAD_SHAPE
+    assert L.velox_pool_keys(C.byref(p), fake, fake, nk, nk - 3, 4, None) == Status.BAD_SHAPE   # past nk
+    assert L.velox_pool_keys(C.byref(p), fake, fake, 100, 90, 11, None) == Status.BAD_SHAPE     # past the cache
+    assert L.velox_pool_keys(C.byref(p), fake, fake, nk, 5, 0, None) == Status.OK               # empty: no launch
+    small_k = headline()
+    small_k.top_k = 1  # pooling does not route: any top_k >= 1 is valid
+    assert L.velox_pool_keys(C.byref(small_k), fake, fake, nk, 5, 0, None) == Status.OK
+    ws = velox.velox_route_workspace_bytes(p)
+    args = lambda kbar, cb, scores=None, w=ws: (C.byref(p), fake, kbar, cb, fake, fake, fake, fake, scores, fake, w,
+                                                None)
+    assert L.velox_route_cached(*args(None, nk)) == Status.NULL_POINTER
+    assert L.velox_route_cached(*args(mis, nk)) == Status.MISALIGNED
+    assert L.velox_route_cached(*args(fake, 48 * 32 - 1)) == Status.BAD_SHAPE       # past rows not covered
+    assert L.velox_route_cached(*args(fake, 48 * 32, fake)) == Status.BAD_SHAPE     # scores need all nk rows
+    assert L.velox_route_cached(*args(fake, nk, None, ws - 1)) == Status.WORKSPACE
+    assert L.velox_route_cached(C.byref(p), fake, fake, nk, None, fake, fake, fake, None, fake, ws,
+                                None) == Status.NULL_POINTER                           # overlap needed when C > 0
     assert L.velox_last_hip_error() == 0
 
 
