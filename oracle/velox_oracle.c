@@ -155,6 +155,68 @@ int velox_oracle_modulate_f32(const float *s, const float *overlap, const uint8_
   return 0;
 }
 
+/* Sign-safe variant of the modulation.  The article says the overlap softly
+ * modulates the model's own importance; read as a probability, that
+ * importance is p_j = softmax_j(s_j) over the row's blocks, and the soft
+ * modulation multiplies it: p_j * (1 + alpha * overlap).  Because the log is
+ * increasing and log p_j = s_j - log(sum_l exp(s_l)) differs from s_j by a
+ * per-row constant, the ranking is the ranking of
+ *   m_j = s_j + log1p(alpha * overlap)
+ * for past blocks of covered rows (current blocks +inf, uncovered rows s_j).
+ * Unlike s * (1 + alpha*o), this never lowers a negative score's rank when
+ * the overlap grows.  fp64 throughout. */
+int velox_oracle_modulate_logprob(const double *s, const float *overlap, const uint8_t *covered, int B, int H,
+                                  int nq, int nk, int blk, int T, int C, double alpha, double *m) {
+  if (!s || !m || !covered || (C > 0 && !overlap) || B < 0 || H < 0 || blk < 1 || T < blk) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)B * H * nq; ++r) {
+    const int64_t b = r / ((int64_t)H * nq);
+    const int i = (int)(r % nq);
+    for (int j = 0; j < nk; ++j) {
+      const int c = (int)(((int64_t)j * blk) / T);
+      const double sv = s[r * nk + j];
+      double mv;
+      if (c >= C)
+        mv = INFINITY;
+      else if (covered[b * nq + i])
+        mv = sv + log1p(alpha * (double)overlap[(b * nq + i) * (int64_t)C + c]);
+      else
+        mv = sv;
+      m[r * nk + j] = mv;
+    }
+  }
+  return 0;
+}
+
+/* The sign-safe variant with the decision in fp32: a = alpha*o in float32,
+ * the log term log1p(a) evaluated in fp64 and rounded once to float32, then
+ * m = s + that term as one float32 addition. */
+int velox_oracle_modulate_logprob_f32(const float *s, const float *overlap, const uint8_t *covered, int B,
+                                      int H, int nq, int nk, int blk, int T, int C, float alpha, double *m) {
+  if (!s || !m || !covered || (C > 0 && !overlap) || B < 0 || H < 0 || blk < 1 || T < blk) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)B * H * nq; ++r) {
+    const int64_t b = r / ((int64_t)H * nq);
+    const int i = (int)(r % nq);
+    for (int j = 0; j < nk; ++j) {
+      const int c = (int)(((int64_t)j * blk) / T);
+      const float sv = s[r * nk + j];
+      float mv;
+      if (c >= C) {
+        mv = INFINITY;
+      } else if (covered[b * nq + i]) {
+        const float ao = alpha * overlap[(b * nq + i) * (int64_t)C + c];
+        const float lt = (float)log1p((double)ao);
+        mv = sv + lt;
+      } else {
+        mv = sv;
+      }
+      m[r * nk + j] = (double)mv;
+    }
+  }
+  return 0;
+}
+
 typedef struct {
   double m;
   int j;

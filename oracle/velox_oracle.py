@@ -35,6 +35,8 @@ def lib():
         L.velox_oracle_scores.argtypes = [_P, _P, _L, _I, _I, _I, _P]
         L.velox_oracle_modulate.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _P]
         L.velox_oracle_modulate_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]
+        L.velox_oracle_modulate_logprob.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _P]
+        L.velox_oracle_modulate_logprob_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]
         L.velox_oracle_select.argtypes = [_P, _L, _I, _I, _P, _P, _P]
         L.velox_oracle_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _L, _I, _I, _P, _P, _I, _L, _P, _P, _P]
         L.velox_oracle_dense_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P]
@@ -90,10 +92,13 @@ def scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
 
 
 def modulate(s: np.ndarray, overlap: np.ndarray, covered: np.ndarray, blk: int, T: int, alpha: float,
-             fp32: bool = False) -> np.ndarray:
+             fp32: bool = False, mode: int = 0) -> np.ndarray:
     """Modulated importance m from s [B,H,nq,nk], overlap [B,nq,C], covered [B,nq].
 
+    ``mode`` 0: m = s*(1 + alpha*o); 1 (sign-safe, probability reading): m = s + log1p(alpha*o).
     ``fp32=True`` takes the decision in float32 (s must then be float32)."""
+    if mode not in (0, 1):
+        raise ValueError(f"unknown modulation mode {mode}")
     B, H, nq, nk = s.shape
     C_ = overlap.shape[-1] if overlap.ndim == 3 else 0
     ov = np.ascontiguousarray(overlap, np.float32)
@@ -102,12 +107,12 @@ def modulate(s: np.ndarray, overlap: np.ndarray, covered: np.ndarray, blk: int, 
     L = lib()
     if fp32:
         s32 = np.ascontiguousarray(s, np.float32)
-        rc = L.velox_oracle_modulate_f32(_ptr(s32), _ptr(ov), _ptr(cov), B, H, nq, nk, blk, T, C_,
-                                         float(np.float32(alpha)), _ptr(m))
+        fn = L.velox_oracle_modulate_logprob_f32 if mode == 1 else L.velox_oracle_modulate_f32
+        rc = fn(_ptr(s32), _ptr(ov), _ptr(cov), B, H, nq, nk, blk, T, C_, float(np.float32(alpha)), _ptr(m))
     else:
         s64 = np.ascontiguousarray(s, np.float64)
-        rc = L.velox_oracle_modulate(_ptr(s64), _ptr(ov), _ptr(cov), B, H, nq, nk, blk, T, C_,
-                                     float(alpha), _ptr(m))
+        fn = L.velox_oracle_modulate_logprob if mode == 1 else L.velox_oracle_modulate
+        rc = fn(_ptr(s64), _ptr(ov), _ptr(cov), B, H, nq, nk, blk, T, C_, float(alpha), _ptr(m))
     _check(rc, "modulate")
     return m
 
@@ -125,13 +130,13 @@ def select(m: np.ndarray, k: int):
 
 
 def route(q: np.ndarray, k: np.ndarray, overlap: np.ndarray, covered: np.ndarray, blk: int, top_k: int,
-          alpha: float) -> dict:
-    """Pool, score, modulate and select for q [B,H,T,d], k [B,H,N,d]."""
+          alpha: float, mode: int = 0) -> dict:
+    """Pool, score, modulate (``mode`` as in modulate) and select for q [B,H,T,d], k [B,H,N,d]."""
     T = q.shape[2]
     qbar = pool(q, blk)
     kbar = pool(k, blk)
     s = scores(qbar, kbar)
-    m = modulate(s, overlap, covered, blk, T, alpha)
+    m = modulate(s, overlap, covered, blk, T, alpha, mode=mode)
     kv_idx, kv_cnt, kth = select(m, top_k)
     return dict(qbar=qbar, kbar=kbar, s=s, m=m, kv_idx=kv_idx, kv_cnt=kv_cnt, kth=kth)
 

@@ -186,6 +186,93 @@ def test_raising_overlap_keeps_positive_blocks():
         assert j in after
 
 
+# ---------------------------------------------------------------- sign-safe (probability) modulation
+
+def test_sign_safe_worked_example():
+    g = golden("ex7_sign_safe.json")
+    C = g["past_chunks"]
+    s = np.asarray(g["s"], np.float64).reshape(1, 1, 1, -1)
+    ov = np.asarray(g["overlap"], np.float32).reshape(1, 1, C)
+    for case, cov in (("covered", 1), ("uncovered", 0)):
+        c = np.full((1, 1), cov, np.uint8)
+        m = O.modulate(s, ov, c, 1, 1, g["alpha"], mode=1)[0, 0, 0]
+        np.testing.assert_allclose(m[:2], [_num(x) for x in g[case]["m"][:2]], rtol=0, atol=1e-15)
+        assert np.isinf(m[2])
+        m32 = O.modulate(s.astype(np.float32), ov, c, 1, 1, g["alpha"], fp32=True, mode=1)[0, 0, 0]
+        assert list(m32) == [_num(x) for x in g[case]["m_fp32"]]
+        for mm in (m[None, None, None], m32[None, None, None]):
+            assert list(O.select(mm, g["top_k"])[0][0, 0, 0]) == g[case]["kv_idx"]
+
+
+def _topk_by_value(v, k):
+    order = sorted(range(len(v)), key=lambda j: (-v[j], j))
+    return sorted(order[:min(k, len(v))])
+
+
+def test_sign_safe_mode_ranks_by_modulated_softmax_probability():
+    """Brute force on the probability form: p_j = softmax(s)_j, importance p_j*(1+alpha*o) on past
+    blocks of covered rows, p_j on uncovered rows, current blocks always kept."""
+    rng = np.random.default_rng(21)
+    B, H, nq, C, blk, T = 2, 2, 3, 5, 2, 4
+    nk = (C + 1) * T // blk
+    for trial in range(20):
+        s = rng.standard_normal((B, H, nq, nk)) * rng.choice([0.3, 2.0, 6.0]) - rng.choice([0.0, 3.0])
+        ov = rng.random((B, nq, C)).astype(np.float32)
+        cov = (rng.random((B, nq)) > 0.3).astype(np.uint8)
+        alpha = float(rng.choice([0.5, 2.0, 7.0]))
+        k = int(rng.integers(T // blk, nk + 1))
+        idx, cnt, _ = O.select(O.modulate(s, ov, cov, blk, T, alpha, mode=1), k)
+        for b, h, i in itertools.product(range(B), range(H), range(nq)):
+            row = s[b, h, i]
+            p = np.exp(row - row.max())
+            p /= p.sum()
+            imp = []
+            for j in range(nk):
+                c = j * blk // T
+                if c >= C:
+                    imp.append(math.inf)
+                elif cov[b, i]:
+                    imp.append(p[j] * (1.0 + alpha * float(ov[b, i, c])))
+                else:
+                    imp.append(p[j])
+            assert list(idx[b, h, i, :cnt[b, h, i]]) == _topk_by_value(imp, k)
+
+
+def test_sign_safe_mode_reduces_to_native_without_modulation():
+    rng = np.random.default_rng(22)
+    B, H, nq, C, blk, T = 1, 2, 3, 4, 2, 4
+    nk = (C + 1) * T // blk
+    s = rng.standard_normal((B, H, nq, nk))
+    ov = rng.random((B, nq, C)).astype(np.float32)
+    native = np.where(np.arange(nk) * blk // T == C, np.inf, s)
+    one = np.ones((B, nq), np.uint8)
+    assert np.array_equal(O.modulate(s, ov, one, blk, T, 0.0, mode=1), native)
+    assert np.array_equal(O.modulate(s, np.zeros_like(ov), one, blk, T, 2.0, mode=1), native)
+    assert np.array_equal(O.modulate(s, ov, np.zeros((B, nq), np.uint8), blk, T, 2.0, mode=1), native)
+
+
+def test_sign_safe_raising_overlap_never_drops_a_block():
+    # unlike s*(1+alpha*o), raising chunk(j)'s overlap keeps j for scores of either sign
+    rng = np.random.default_rng(23)
+    C, blk, T, k = 6, 1, 1, 4
+    nk = C + 1
+    checked_negative = 0
+    for _ in range(300):
+        s = rng.standard_normal((1, 1, 1, nk)) - 0.5
+        ov = rng.random((1, 1, C)).astype(np.float32)
+        cov = np.ones((1, 1), np.uint8)
+        before = set(O.select(O.modulate(s, ov, cov, blk, T, 1.5, mode=1), k)[0][0, 0, 0])
+        j = int(rng.integers(0, C))
+        if j not in before:
+            continue
+        checked_negative += s[0, 0, 0, j] < 0
+        ov2 = ov.copy()
+        ov2[0, 0, j] = min(1.0, ov2[0, 0, j] + 0.5)
+        after = set(O.select(O.modulate(s, ov2, cov, blk, T, 1.5, mode=1), k)[0][0, 0, 0])
+        assert j in after
+    assert checked_negative > 10
+
+
 # ---------------------------------------------------------------- attention
 
 def test_two_key_closed_form():
