@@ -189,12 +189,34 @@ def main():
                                    "attention_speedup_vs_keep_all": round(keep_all_ms / attn_avg, 3),
                                    "layer_speedup_vs_keep_all": round(keep_all_ms / ms_step, 3)}
 
+    res["route_log_prob"] = bench_route_log_prob(velox, cfg, q, k, ov, cov, kv_idx, ws, stream)
     res["route_cached"] = bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el,
                                              x.overlap.nbytes + x.covered.nbytes + gi.nbytes + cnt.nbytes)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def bench_route_log_prob(velox, cfg, q, k, ov, cov, kv_idx, ws, stream, reps=20):
+    """velox_route with the sign-safe (log-probability) modulation: same kernels and bytes,
+    different modulation arithmetic in the select kernel."""
+    import torch
+    idx2 = torch.empty_like(kv_idx)
+    cnt2 = torch.empty((cfg.batch, cfg.heads, cfg.nq), dtype=torch.int32, device="cuda")
+    call = lambda: velox.route(q, k, ov, cov, cfg.block, cfg.top_k, cfg.alpha, out=(idx2, cnt2), workspace=ws,
+                               modulation=velox.MOD_LOG_PROB)
+    call()
+    torch.cuda.synchronize()
+    changed = int((idx2 != kv_idx).any(dim=-1).sum())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms": round(e0.elapsed_time(e1) / reps, 4), "rows_with_different_list": changed,
+            "rows": cfg.rows}
 
 
 def bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el, small_bytes, reps=20):

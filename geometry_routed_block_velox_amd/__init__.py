@@ -30,6 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libvelox.so")
 
 VELOX_F32, VELOX_BF16 = 0, 1
+MOD_SCALE, MOD_LOG_PROB = 0, 1   # velox_modulation
 MAX_QUERY_BLOCKS, MAX_KV_BLOCKS = 64, 8192
 
 
@@ -51,7 +52,7 @@ class Problem(C.Structure):
     _fields_ = [
         ("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32), ("chunk_tokens", C.c_int32),
         ("past_chunks", C.c_int32), ("block", C.c_int32), ("top_k", C.c_int32), ("alpha", C.c_float),
-        ("dtype", C.c_int32),
+        ("dtype", C.c_int32), ("modulation", C.c_int32),
     ]
 
     @property
@@ -153,21 +154,22 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-def problem_for(q_shape, kv_tokens: int, block: int, top_k: int, alpha: float, dtype: int) -> Problem:
+def problem_for(q_shape, kv_tokens: int, block: int, top_k: int, alpha: float, dtype: int,
+                modulation: int = MOD_SCALE) -> Problem:
     """Build a Problem from Q's shape [B,H,T,d] and the KV length N = (C+1)*T."""
     B, H, T, d = q_shape
     if T <= 0 or kv_tokens % T:
         raise ValueError(f"KV length {kv_tokens} is not a whole number of chunks of {T} tokens")
-    return Problem(B, H, d, T, kv_tokens // T - 1, block, top_k, float(alpha), dtype)
+    return Problem(B, H, d, T, kv_tokens // T - 1, block, top_k, float(alpha), dtype, modulation)
 
 
 def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_scores: bool = False,
-          out=None, workspace=None, stream=None):
+          out=None, workspace=None, stream=None, modulation: int = MOD_SCALE):
     """velox_route: returns (kv_idx [B,H,nq,top_k] int32, kv_cnt [B,H,nq] int32[, scores fp32])."""
     torch = _torch()
     _dev(q, "q", ndim=4)
     _dev(k, "k", q.dtype, ndim=4)
-    p = problem_for(tuple(q.shape), k.shape[2], block, top_k, alpha, _dtype_code(q))
+    p = problem_for(tuple(q.shape), k.shape[2], block, top_k, alpha, _dtype_code(q), modulation)
     _raise(velox_check(p), "velox_route")
     B, H, T, d = q.shape
     if tuple(k.shape) != (B, H, k.shape[2], d):
@@ -218,13 +220,13 @@ def pool_keys(k, chunk_tokens: int, block: int, first_block: int, num_blocks: in
 
 
 def route_cached(q, kbar, past_chunks: int, overlap, covered, block: int, top_k: int, alpha: float,
-                 return_scores: bool = False, out=None, workspace=None, stream=None):
+                 return_scores: bool = False, out=None, workspace=None, stream=None, modulation: int = MOD_SCALE):
     """velox_route_cached: route from pooled keys kbar [B,H,cache_blocks,d] (float32) instead of K."""
     torch = _torch()
     _dev(q, "q", ndim=4)
     _dev(kbar, "kbar", torch.float32, ndim=4)
     B, H, T, d = q.shape
-    p = problem_for(tuple(q.shape), (past_chunks + 1) * T, block, top_k, alpha, _dtype_code(q))
+    p = problem_for(tuple(q.shape), (past_chunks + 1) * T, block, top_k, alpha, _dtype_code(q), modulation)
     _raise(velox_check(p), "velox_route_cached")
     if tuple(kbar.shape[:2]) != (B, H) or kbar.shape[3] != d:
         raise ValueError(f"kbar shape {tuple(kbar.shape)} does not match q {tuple(q.shape)}")
@@ -253,14 +255,15 @@ def route_cached(q, kbar, past_chunks: int, overlap, covered, block: int, top_k:
     return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
 
 
-def select(scores, overlap, covered, block: int, top_k: int, alpha: float, stream=None):
+def select(scores, overlap, covered, block: int, top_k: int, alpha: float, stream=None,
+           modulation: int = MOD_SCALE):
     """velox_select: modulation + top-k from given scores [B,H,nq,nk] (float32)."""
     torch = _torch()
     _dev(scores, "scores", torch.float32, ndim=4)
     B, H, nq, nk = scores.shape
     if nk % nq:
         raise ValueError("nk must be a whole number of chunks of nq blocks")
-    p = Problem(B, H, 64, nq * block, nk // nq - 1, block, top_k, float(alpha), VELOX_F32)
+    p = Problem(B, H, 64, nq * block, nk // nq - 1, block, top_k, float(alpha), VELOX_F32, modulation)
     _raise(velox_check(p), "velox_select")
     if p.past_chunks > 0:
         _dev(overlap, "overlap", torch.float32)

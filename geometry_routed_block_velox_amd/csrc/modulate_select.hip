@@ -7,7 +7,9 @@
 //   m_j = +inf                                  if block j is in the current chunk
 //       = s_j * (1 + alpha * overlap[b,i,c(j)]) if the row is covered
 //       = s_j                                   otherwise
-// (each operation a separately rounded float32 operation), then keep the
+// (each operation a separately rounded float32 operation), or, in the
+// sign-safe mode that reads the importance as the softmax probability of
+// s_j, m_j = s_j + log1p(alpha * overlap) for covered past blocks; then keep the
 // k_eff largest m_j with ties to the lower index, written in ascending order.
 //
 // One workgroup (256 threads) per row.  The m_j become order-preserving
@@ -28,6 +30,16 @@ __device__ __forceinline__ float modulated(float s, float alpha, float o) {
   const float a = alpha * o;
   const float f = 1.0f + a;
   return s * f;
+}
+
+// Sign-safe mode: p_j * (1 + alpha*o) with p_j = softmax(s)_j ranks like this.
+// log1p runs in float64 and is rounded once, so the term does not depend on
+// the float32 log1p's last-bit behaviour.
+__device__ __forceinline__ float modulated_log_prob(float s, float alpha, float o) {
+#pragma clang fp contract(off)
+  const float a = alpha * o;
+  const float lt = (float)log1p((double)a);
+  return s + lt;
 }
 
 __device__ __forceinline__ uint32_t order_key(float m) {
@@ -63,7 +75,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int* tmp) {
 __global__ __launch_bounds__(kThreads) void modulate_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ overlap, const uint8_t* __restrict__ covered,
     int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt, int H, int nq, int nk, int blk, int T, int C,
-    float alpha, int top_k, int keff) {
+    float alpha, int top_k, int keff, int log_prob) {
   extern __shared__ uint32_t keys[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sel_digit, sel_above;
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void modulate_select_kernel(
     if (c >= C)
       m = __builtin_inff();
     else if (cov)
-      m = modulated(srow[j], alpha, orow[c]);
+      m = log_prob ? modulated_log_prob(srow[j], alpha, orow[c]) : modulated(srow[j], alpha, orow[c]);
     else
       m = srow[j];
     keys[j] = order_key(m);
@@ -167,7 +179,7 @@ hipError_t launch_modulate_select(const velox_problem& p, const float* scores, c
   const int rows = x.B * x.H * x.nq;
   hipLaunchKernelGGL(modulate_select_kernel, dim3(rows), dim3(kThreads), (size_t)x.nk * sizeof(uint32_t), s,
                      scores, overlap, covered, kv_idx, kv_cnt, x.H, x.nq, x.nk, x.blk, x.T, x.C, p.alpha, x.top_k,
-                     x.k_eff);
+                     x.k_eff, p.modulation == VELOX_MOD_LOG_PROB ? 1 : 0);
   return hipGetLastError();
 }
 

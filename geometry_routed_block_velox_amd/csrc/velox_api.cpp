@@ -29,6 +29,7 @@ velox_status check_problem(const velox_problem* p, bool routing) {
     return VELOX_ERR_BAD_SHAPE;
   if (p->chunk_tokens % p->block) return VELOX_ERR_BAD_SHAPE;
   if (!isfinite(p->alpha) || p->alpha < 0.f) return VELOX_ERR_BAD_SHAPE;
+  if (p->modulation != VELOX_MOD_SCALE && p->modulation != VELOX_MOD_LOG_PROB) return VELOX_ERR_BAD_SHAPE;
   if (p->dtype != VELOX_F32 && p->dtype != VELOX_BF16) return VELOX_ERR_UNSUPPORTED;
   if ((p->head_dim != 64 && p->head_dim != 128) || (p->block != 64 && p->block != 128))
     return VELOX_ERR_UNSUPPORTED;

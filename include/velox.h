@@ -49,7 +49,8 @@ typedef struct ihipStream_t *velox_stream_t;
 typedef enum velox_status {
   VELOX_OK = 0,
   VELOX_ERR_NULL_POINTER = 1, /* a required pointer is NULL                                  */
-  VELOX_ERR_BAD_SHAPE = 2,    /* sizes < 1, T % blk != 0, top_k < ncur, alpha < 0 or not finite */
+  VELOX_ERR_BAD_SHAPE = 2,    /* sizes < 1, T % blk != 0, top_k < ncur, alpha < 0 or not finite,
+                                 unknown modulation                                          */
   VELOX_ERR_UNSUPPORTED = 3,  /* (dtype, d, blk) not built, or nq / nk above the limits below */
   VELOX_ERR_MISALIGNED = 4,   /* Q, K, V or Out not 16-byte aligned                          */
   VELOX_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than velox_route_workspace_bytes  */
@@ -57,6 +58,19 @@ typedef enum velox_status {
 } velox_status;
 
 typedef enum velox_dtype { VELOX_F32 = 0, VELOX_BF16 = 1 } velox_dtype;
+
+/* How the overlap modulates the importance of a past block j of a covered
+ * row (both readings of the article's Deep analysis: the overlap softly
+ * modulates, and does not replace, the model's own block importance):
+ *   VELOX_MOD_SCALE     m_j = s_j * (1 + alpha * o)       the literal reading;
+ *                       for s_j < 0 a larger overlap lowers m_j.
+ *   VELOX_MOD_LOG_PROB  m_j = s_j + log1p(alpha * o)      the importance read as
+ *                       the softmax probability p_j of s_j: p_j*(1 + alpha*o)
+ *                       ranks exactly like this, so a larger overlap never
+ *                       lowers a block's rank whatever the sign of s_j.
+ * In float32: alpha*o, then log1p in float64 rounded once to float32, then
+ * one float32 addition. */
+typedef enum velox_modulation { VELOX_MOD_SCALE = 0, VELOX_MOD_LOG_PROB = 1 } velox_modulation;
 
 /* Built configurations: d in {64, 128}, blk in {64, 128}, both dtypes.
  * Limits: nq <= VELOX_MAX_QUERY_BLOCKS, nk <= VELOX_MAX_KV_BLOCKS. */
@@ -75,6 +89,8 @@ typedef struct velox_problem {
                            (top_k >= ncur); values above nk keep every block               */
   float alpha;          /* modulation strength, finite and >= 0                            */
   velox_dtype dtype;    /* element type of Q, K, V and Out                                 */
+  int32_t modulation;   /* a velox_modulation (0 = VELOX_MOD_SCALE when zero-initialised);
+                           used by routing, must be valid everywhere                       */
 } velox_problem;
 
 /* Validate a problem on the host (no GPU needed).  Returns VELOX_OK,
@@ -105,8 +121,9 @@ size_t velox_route_workspace_bytes(const velox_problem *p);
  *
  * Per row (b,h,i): qbar_i and kbar_j are the means of Q over query block i
  * and of K over KV block j (float32 sums); s_j = <qbar_i, kbar_j>/sqrt(d);
- * m_j = +inf for current-chunk blocks, s_j*(1 + alpha*overlap[b,i,chunk(j)])
- * for past blocks of covered rows, s_j otherwise (every operation a
+ * m_j = +inf for current-chunk blocks, the modulated importance of
+ * p->modulation with o = overlap[b,i,chunk(j)] for past blocks of covered
+ * rows (s_j*(1 + alpha*o) by default), s_j otherwise (every operation a
  * separately rounded float32 operation).  The kept set is the k_eff largest
  * m_j, ties broken toward the lower block index (-0 equals +0). */
 velox_status velox_route(const velox_problem *p, const void *q, const void *k, const float *overlap,

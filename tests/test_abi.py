@@ -128,6 +128,20 @@ def test_cache_entry_points_validate_before_launch():
     assert L.velox_last_hip_error() == 0
 
 
+def test_modulation_mode_is_validated():
+    p = headline()
+    assert p.modulation == velox.MOD_SCALE          # zero-initialised default
+    p.modulation = velox.MOD_LOG_PROB
+    assert velox.velox_check(p) == Status.OK
+    for bad in (2, -1, 7):
+        p.modulation = bad
+        assert velox.velox_check(p) == Status.BAD_SHAPE
+        assert velox.velox_route_workspace_bytes(p) == 0
+    fake = C.c_void_p(0x100000)
+    assert velox.lib().velox_sparse_attn(C.byref(p), fake, fake, fake, fake, fake, fake, None,
+                                         None) == Status.BAD_SHAPE
+
+
 def test_status_strings():
     L = velox.lib()
     for s in range(7):

@@ -127,3 +127,40 @@ def test_end_to_end_layer(name):
     say(f"{name}: end-to-end on {toks.size} tokens ({(~same_row).sum()} rows with in-band swaps)")
     ref, _ = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block, tokens=toks)
     check_close(out_to_f64(out).reshape(-1, cfg.head_dim)[toks], ref, *tol(cfg))
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_route_sign_safe_mode_matches_oracle(name):
+    """Sign-safe modulation (s + log1p(alpha*o)) against the oracle's fp64 mode 1: gap rule."""
+    x = cached_inputs(name)
+    cfg = x.cfg
+    d = dev_inputs(x)
+    say(f"{name}: velox_route, log-probability modulation")
+    kv_idx, kv_cnt = velox.route(d["q"], d["k"], d["overlap"], d["covered"], cfg.block, cfg.top_k, cfg.alpha,
+                                 modulation=velox.MOD_LOG_PROB)
+    lit_idx, _ = velox.route(d["q"], d["k"], d["overlap"], d["covered"], cfg.block, cfg.top_k, cfg.alpha)
+    torch.cuda.synchronize()
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha, mode=1)
+    st = check_selection(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), r["m"], r["kth"], r["kv_idx"], cfg.k_eff,
+                         cfg.nk - cfg.ncur)
+    changed = int((kv_idx != lit_idx).any(dim=-1).sum())
+    say(f"{name}: selection {st}; rows whose list differs from the literal mode: {changed} of {cfg.rows}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "headline"])
+def test_select_sign_safe_decision_is_bit_exact(name):
+    cfg = get_config(name)
+    rng = np.random.default_rng(12)
+    B, H, nq, nk = cfg.batch, cfg.heads, cfg.nq, cfg.nk
+    s = (rng.standard_normal((B, H, nq, nk)) - 0.5).astype(np.float32)
+    s[..., ::7] = -0.25
+    s[..., 3::11] = -0.0
+    ov = rng.random((B, nq, cfg.past_chunks)).astype(np.float32)
+    ov[:, :, ::3] = 0.0
+    cov = (rng.random((B, nq)) > 0.3).astype(np.uint8)
+    say(f"{name}: velox_select, log-probability modulation")
+    kv_idx, kv_cnt = velox.select(to_dev(s), to_dev(ov), to_dev(cov), cfg.block, cfg.top_k, cfg.alpha,
+                                  modulation=velox.MOD_LOG_PROB)
+    m = O.modulate(s, ov, cov, cfg.block, cfg.chunk_tokens, cfg.alpha, fp32=True, mode=1)
+    ref_idx, ref_cnt, _ = O.select(m, cfg.top_k)
+    assert np.array_equal(kv_idx.cpu().numpy(), ref_idx) and np.array_equal(kv_cnt.cpu().numpy(), ref_cnt)
