@@ -193,9 +193,48 @@ def main():
     res["route_cached"] = bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el,
                                              x.overlap.nbytes + x.covered.nbytes + gi.nbytes + cnt.nbytes)
 
+    res["split_kv_small"] = bench_split_small(velox, stream)
+
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def bench_split_small(velox, stream, reps=50):
+    """Split-KV attention on the Small workload (64 rows for 256 CUs): one workgroup per
+    row against velox_sparse_attn_split with the automatic split count."""
+    import numpy as np
+    import torch
+    from synth import get_config, make_inputs
+    cfg = get_config("small")
+    x = make_inputs(cfg)
+    up = lambda a: (torch.from_numpy(a).view(torch.int16).view(torch.bfloat16) if a.dtype == np.uint16
+                    else torch.from_numpy(a)).cuda()
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    kv_idx, kv_cnt = velox.route(q, k, up(x.overlap), up(x.covered), cfg.block, cfg.top_k, cfg.alpha)
+    p = velox.problem_for(tuple(q.shape), k.shape[2], cfg.block, cfg.top_k, cfg.alpha, velox.VELOX_BF16)
+    n = velox.auto_splits(p)
+    ws = torch.empty(max(velox.velox_sparse_attn_split_workspace_bytes(p, n), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(kv_cnt.sum())
+
+    def timed(splits):
+        for _ in range(3):
+            velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out, splits=splits, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out, splits=splits, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t1, ts = timed(None), timed(n)
+    return {"workload": f"small: B1 H4 d64 T1024 chunk12 blk64 top-k48 ({cfg.rows} rows)", "splits": n,
+            "unsplit_ms": round(t1, 4), "split_ms": round(ts, 4), "speedup": round(t1 / ts, 3),
+            "unsplit_tflops": round(f_exec / (t1 * 1e-3) / 1e12, 2),
+            "split_tflops": round(f_exec / (ts * 1e-3) / 1e12, 2),
+            "split_frac_of_peak": round(f_exec / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_route_log_prob(velox, cfg, q, k, ov, cov, kv_idx, ws, stream, reps=20):

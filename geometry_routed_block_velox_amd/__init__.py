@@ -13,7 +13,7 @@ Entry points (same names as the C ABI):
   pool_keys(k, chunk_tokens, block, first_block, num_blocks, ...) -> kbar cache
   route_cached(q, kbar, past_chunks, overlap, covered, block, top_k, alpha, ...) -> as route
   select(scores, overlap, covered, block, top_k, alpha) -> (kv_idx, kv_cnt)
-  sparse_attn(q, k, v, kv_idx, kv_cnt, block, ...) -> out[, lse]
+  sparse_attn(q, k, v, kv_idx, kv_cnt, block, ..., splits=None|n|"auto") -> out[, lse]
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
-    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached",
+    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +93,12 @@ def lib():
         L.velox_select.restype = C.c_int
         L.velox_sparse_attn.argtypes = [P, V, V, V, V, V, V, V, V]
         L.velox_sparse_attn.restype = C.c_int
+        L.velox_sparse_attn_split_workspace_bytes.argtypes = [P, C.c_int32]
+        L.velox_sparse_attn_split_workspace_bytes.restype = C.c_size_t
+        L.velox_sparse_attn_auto_splits.argtypes = [P, C.c_int32]
+        L.velox_sparse_attn_auto_splits.restype = C.c_int32
+        L.velox_sparse_attn_split.argtypes = [P, V, V, V, V, V, C.c_int32, V, V, V, C.c_size_t, V]
+        L.velox_sparse_attn_split.restype = C.c_int
         L.velox_status_string.argtypes = [C.c_int]
         L.velox_status_string.restype = C.c_char_p
         L.velox_last_hip_error.argtypes = []
@@ -107,6 +113,10 @@ def velox_check(p: Problem) -> int:
 
 def velox_route_workspace_bytes(p: Problem) -> int:
     return lib().velox_route_workspace_bytes(C.byref(p))
+
+
+def velox_sparse_attn_split_workspace_bytes(p: Problem, num_splits: int) -> int:
+    return lib().velox_sparse_attn_split_workspace_bytes(C.byref(p), int(num_splits))
 
 
 def _raise(status: int, where: str):
@@ -282,8 +292,19 @@ def select(scores, overlap, covered, block: int, top_k: int, alpha: float, strea
     return kv_idx, kv_cnt
 
 
-def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, out=None, stream=None):
-    """velox_sparse_attn: returns out [B,H,T,d] (dtype of q)[, lse [B,H,T] float32]."""
+def auto_splits(p: Problem, num_cus: int | None = None) -> int:
+    """velox_sparse_attn_auto_splits for the current device's compute-unit count."""
+    if num_cus is None:
+        num_cus = _torch().cuda.get_device_properties(_torch().cuda.current_device()).multi_processor_count
+    return int(lib().velox_sparse_attn_auto_splits(C.byref(p), int(num_cus)))
+
+
+def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, out=None, stream=None,
+                splits=None, workspace=None):
+    """velox_sparse_attn: returns out [B,H,T,d] (dtype of q)[, lse [B,H,T] float32].
+
+    ``splits``: None = one workgroup per row (velox_sparse_attn); an int or "auto" =
+    velox_sparse_attn_split with that many list segments per row."""
     torch = _torch()
     _dev(q, "q", ndim=4)
     _dev(k, "k", q.dtype, ndim=4)
@@ -298,7 +319,16 @@ def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, o
         raise ValueError("kv_idx/kv_cnt shape mismatch")
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib().velox_sparse_attn(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
-                                 _ptr(lse), _stream(stream))
-    _raise(st, "velox_sparse_attn")
+    if splits is None:
+        st = lib().velox_sparse_attn(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
+                                     _ptr(lse), _stream(stream))
+        _raise(st, "velox_sparse_attn")
+    else:
+        n = auto_splits(p) if splits == "auto" else int(splits)
+        need = velox_sparse_attn_split_workspace_bytes(p, n)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        st = lib().velox_sparse_attn_split(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), n,
+                                           _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+        _raise(st, "velox_sparse_attn_split")
     return (o, lse) if return_lse else o

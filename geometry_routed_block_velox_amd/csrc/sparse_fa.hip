@@ -293,11 +293,33 @@ __device__ __forceinline__ void run_pass(WaveState<D, BLK>& w, uint4 (*stages)[2
   }
 }
 
+// Split-KV: with `splits` > 0 workgroup g handles segment g % splits of row
+// g / splits, the list positions [s*cnt/splits, (s+1)*cnt/splits), and
+// writes a float32 partial result (normalised output and natural-log LSE of
+// its segment) that merge_splits_kernel combines.  splits == 0: the whole
+// row, written directly.
+struct Segment {
+  int row, begin, count, part;
+};
+
+__device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* __restrict__ kv_cnt, int top_k) {
+  Segment sg;
+  const int parts = splits > 0 ? splits : 1;
+  sg.row = g / parts;
+  sg.part = g;
+  const int cnt = min(max(kv_cnt[sg.row], 0), top_k);
+  const int s = g % parts;
+  sg.begin = (int)(((long long)s * cnt) / parts);
+  sg.count = (int)(((long long)(s + 1) * cnt) / parts) - sg.begin;
+  return sg;
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2) {
+    float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   using F = Fa<D, BLK>;
   __shared__ uint4 stages[2][2 * F::TILE_CHUNKS];
 
@@ -306,15 +328,16 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
   const int qg = wave & 1, kg = wave >> 1;
   const int qc = lane & 31, hh = lane >> 5;
   const int kbase = kg * F::KW;
-  const int row = xcd_grouped(blockIdx.x, gridDim.x);
+  const Segment sg = segment_of(xcd_grouped(blockIdx.x, gridDim.x), splits, kv_cnt, top_k);
+  const int row = sg.row;
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
   const uint16_t* kh = k + (size_t)bh * N * D;
   const uint16_t* vh = v + (size_t)bh * N * D;
   // The list is read-only here and wave-uniform: scalar loads via the constant address space.
   const __attribute__((address_space(4))) int32_t* list =
-      (const __attribute__((address_space(4))) int32_t*)(kv_idx + (size_t)row * top_k);
-  const int cnt = min(max(kv_cnt[row], 0), top_k);
+      (const __attribute__((address_space(4))) int32_t*)(kv_idx + (size_t)row * top_k + sg.begin);
+  const int cnt = sg.count;
 
   WaveState<D, BLK> w;
   const size_t qrow0 = (size_t)bh * nq * BLK + (size_t)iq * BLK + qg * F::QW;
@@ -384,7 +407,10 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
       const float lt = lw[qt] * a0 + l1 * a1;
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const size_t tq = qrow0 + 32 * qt + qc;
+      // split mode: float32 partial result of this segment, token t of the block
+      const size_t pt = ((size_t)sg.part * BLK + qg * F::QW + 32 * qt + qc);
       uint16_t* orow = out + tq * D;
+      float* prow = part_o + pt * D;
 #pragma unroll
       for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
@@ -396,14 +422,24 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
             const float o1 = xo[(((qg * F::DT + dt) * F::QT + qt) * 16 + r) * 64 + lane];
             o[e] = (w.oacc[dt][qt][r] * a0 + o1 * a1) * inv;
           }
-          uint2 pk;
-          pk.x = pack_bf16x2(o[0], o[1]);
-          pk.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * hh) = pk;
+          if (splits) {
+            *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * hh) = make_float4(o[0], o[1], o[2], o[3]);
+          } else {
+            uint2 pk;
+            pk.x = pack_bf16x2(o[0], o[1]);
+            pk.y = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * hh) = pk;
+          }
         }
       }
-      if (lse && hh == 0)
-        lse[tq] = lt > 0.f ? (mm * scale_log2 + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+      const float row_lse =
+          lt > 0.f ? (mm * scale_log2 + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+      if (hh == 0) {
+        if (splits)
+          part_lse[pt] = row_lse;
+        else if (lse)
+          lse[tq] = row_lse;
+      }
     }
   }
 }
@@ -416,18 +452,21 @@ __global__ __launch_bounds__(BLK) void sparse_fa_f32_kernel(const float* __restr
                                                             const int32_t* __restrict__ kv_idx,
                                                             const int32_t* __restrict__ kv_cnt,
                                                             float* __restrict__ out, float* __restrict__ lse,
-                                                            int nq, int nk, int top_k, float scale_log2) {
+                                                            int nq, int nk, int top_k, float scale_log2, int splits,
+                                                            float* __restrict__ part_o,
+                                                            float* __restrict__ part_lse) {
   extern __shared__ float fs[];
   float* kt = fs;
   float* vt = fs + BLK * D;
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;
+  const Segment sg = segment_of(blockIdx.x, splits, kv_cnt, top_k);
+  const int row = sg.row;
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
   const float* kh = k + (size_t)bh * N * D;
   const float* vh = v + (size_t)bh * N * D;
-  const int32_t* list = kv_idx + (size_t)row * top_k;
-  const int cnt = min(max(kv_cnt[row], 0), top_k);
+  const int32_t* list = kv_idx + (size_t)row * top_k + sg.begin;
+  const int cnt = sg.count;
   const size_t tq = (size_t)bh * nq * BLK + (size_t)iq * BLK + tid;
 
   float qv[D], o[D];
@@ -466,26 +505,85 @@ __global__ __launch_bounds__(BLK) void sparse_fa_f32_kernel(const float* __restr
     }
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  const float row_lse = l_run > 0.f ? (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+  float* orow = splits ? part_o + ((size_t)sg.part * BLK + tid) * D : out + tq * D;
 #pragma unroll
-  for (int e = 0; e < D; ++e) out[tq * D + e] = o[e] * inv;
-  if (lse) lse[tq] = l_run > 0.f ? (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+  for (int e = 0; e < D; ++e) orow[e] = o[e] * inv;
+  if (splits)
+    part_lse[(size_t)sg.part * BLK + tid] = row_lse;
+  else if (lse)
+    lse[tq] = row_lse;
 }
 
+// Combine the segments of every row: with L_s the segment LSEs and O_s their
+// normalised outputs, LSE = log sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s
+// (segments without a valid block have L_s = -inf and weight 0).  One thread
+// per output element; grid = ceil(rows * BLK * D / 256).
+template <int D, int BLK, bool OUT_BF16>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse, int splits,
+                                                           long long n_elem, void* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_elem) return;
+  const long long tok = e / D;  // = row * BLK + t, also the output token index
+  const int d = (int)(e % D);
+  const long long row = tok / BLK;
+  const int t = (int)(tok % BLK);
+  const float* pl = part_lse + row * splits * BLK + t;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(size_t)s * BLK]);
+  float acc = 0.f, wsum = 0.f;
+  if (mx > -__builtin_inff()) {
+    const float* po = part_o + (row * splits * BLK + t) * D + d;
+    for (int s = 0; s < splits; ++s) {
+      const float ls = pl[(size_t)s * BLK];
+      if (ls == -__builtin_inff()) continue;
+      const float w = __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
+      wsum += w;
+      acc += w * po[(size_t)s * BLK * D];
+    }
+  }
+  const float o = wsum > 0.f ? acc / wsum : 0.f;
+  if (OUT_BF16) {
+    const __bf16 b = (__bf16)o;
+    uint16_t u;
+    __builtin_memcpy(&u, &b, 2);
+    static_cast<uint16_t*>(out)[e] = u;
+  } else {
+    static_cast<float*>(out)[e] = o;
+  }
+  if (lse && d == 0) lse[tok] = wsum > 0.f ? mx + __builtin_logf(wsum) : -__builtin_inff();
+}
+
+// Launchers: splits == 0 writes out/lse directly; otherwise partial results go
+// to part_o/part_lse and merge_splits_kernel writes out/lse.
 template <int D, int BLK>
 hipError_t fa_bf16(const Dims& x, const void* q, const void* k, const void* v, const int32_t* kv_idx,
-                   const int32_t* kv_cnt, void* out, float* lse, hipStream_t s) {
+                   const int32_t* kv_cnt, void* out, float* lse, int splits, float* part_o, float* part_lse,
+                   hipStream_t s) {
   const int rows = x.B * x.H * x.nq;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((sparse_fa_bf16_kernel<D, BLK>), dim3(rows), dim3(Fa<D, BLK>::NT), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipLaunchKernelGGL((sparse_fa_bf16_kernel<D, BLK>), dim3(rows * (splits > 0 ? splits : 1)), dim3(Fa<D, BLK>::NT),
+                     0, s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), kv_idx, kv_cnt, static_cast<uint16_t*>(out), lse, x.nq, x.nk,
-                     x.top_k, scale_log2);
+                     x.top_k, scale_log2, splits, part_o, part_lse);
+  return hipGetLastError();
+}
+
+template <int D, int BLK, bool OUT_BF16>
+hipError_t merge(const Dims& x, int splits, const float* part_o, const float* part_lse, void* out, float* lse,
+                 hipStream_t s) {
+  const long long n = (long long)x.B * x.H * x.nq * BLK * D;
+  hipLaunchKernelGGL((merge_splits_kernel<D, BLK, OUT_BF16>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     part_o, part_lse, splits, n, out, lse);
   return hipGetLastError();
 }
 
 template <int D, int BLK>
 hipError_t fa_f32(const Dims& x, const void* q, const void* k, const void* v, const int32_t* kv_idx,
-                  const int32_t* kv_cnt, void* out, float* lse, hipStream_t s) {
+                  const int32_t* kv_cnt, void* out, float* lse, int splits, float* part_o, float* part_lse,
+                  hipStream_t s) {
   auto kern = sparse_fa_f32_kernel<D, BLK>;
   const size_t lds = 2 * (size_t)BLK * D * sizeof(float);
   // Thread-safe one-time opt-in to more than 64 KiB of dynamic LDS.
@@ -494,23 +592,28 @@ hipError_t fa_f32(const Dims& x, const void* q, const void* k, const void* v, co
   if (attr != hipSuccess) return attr;
   const int rows = x.B * x.H * x.nq;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(kern, dim3(rows), dim3(BLK), lds, s, static_cast<const float*>(q),
+  hipLaunchKernelGGL(kern, dim3(rows * (splits > 0 ? splits : 1)), dim3(BLK), lds, s, static_cast<const float*>(q),
                      static_cast<const float*>(k), static_cast<const float*>(v), kv_idx, kv_cnt,
-                     static_cast<float*>(out), lse, x.nq, x.nk, x.top_k, scale_log2);
+                     static_cast<float*>(out), lse, x.nq, x.nk, x.top_k, scale_log2, splits, part_o, part_lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sparse_attn(const velox_problem& p, const void* q, const void* k, const void* v,
-                              const int32_t* kv_idx, const int32_t* kv_cnt, void* out, float* lse,
-                              hipStream_t s) {
+                              const int32_t* kv_idx, const int32_t* kv_cnt, void* out, float* lse, int splits,
+                              float* part_o, float* part_lse, hipStream_t s) {
   const Dims x = dims(p);
   const bool bf = p.dtype == VELOX_BF16;
-#define VELOX_FA(Dv, Bv)                                                          \
-  if (p.head_dim == Dv && p.block == Bv)                                          \
-    return bf ? fa_bf16<Dv, Bv>(x, q, k, v, kv_idx, kv_cnt, out, lse, s)          \
-              : fa_f32<Dv, Bv>(x, q, k, v, kv_idx, kv_cnt, out, lse, s);
+#define VELOX_FA(Dv, Bv)                                                                                       \
+  if (p.head_dim == Dv && p.block == Bv) {                                                                     \
+    hipError_t e = bf ? fa_bf16<Dv, Bv>(x, q, k, v, kv_idx, kv_cnt, out, lse, splits, part_o, part_lse, s)      \
+                      : fa_f32<Dv, Bv>(x, q, k, v, kv_idx, kv_cnt, out, lse, splits, part_o, part_lse, s);      \
+    if (e == hipSuccess && splits > 0)                                                                         \
+      e = bf ? merge<Dv, Bv, true>(x, splits, part_o, part_lse, out, lse, s)                                   \
+             : merge<Dv, Bv, false>(x, splits, part_o, part_lse, out, lse, s);                                 \
+    return e;                                                                                                  \
+  }
   VELOX_FA(128, 128)
   VELOX_FA(128, 64)
   VELOX_FA(64, 128)

@@ -135,7 +135,47 @@ velox_status velox_sparse_attn(const velox_problem* p, const void* q, const void
   if (st != VELOX_OK) return st;
   if (!q || !k || !v || !kv_idx || !kv_cnt || !out) return VELOX_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VELOX_ERR_MISALIGNED;
-  return hip_status(velox::launch_sparse_attn(*p, q, k, v, kv_idx, kv_cnt, out, lse,
+  return hip_status(velox::launch_sparse_attn(*p, q, k, v, kv_idx, kv_cnt, out, lse, 0, nullptr, nullptr,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t velox_sparse_attn_split_workspace_bytes(const velox_problem* p, int32_t num_splits) {
+  if (check_problem(p, false) != VELOX_OK || num_splits < 1 || num_splits > VELOX_MAX_SPLITS) return 0;
+  const velox::Dims x = velox::dims(*p);
+  const size_t parts = (size_t)x.B * x.H * x.nq * num_splits;
+  return align256(parts * x.blk * x.d * sizeof(float)) + align256(parts * x.blk * sizeof(float));
+}
+
+int32_t velox_sparse_attn_auto_splits(const velox_problem* p, int32_t num_cus) {
+  if (check_problem(p, false) != VELOX_OK || num_cus < 1) return 1;
+  const velox::Dims x = velox::dims(*p);
+  const int64_t rows = (int64_t)x.B * x.H * x.nq;
+  if (rows >= num_cus) return 1;
+  // About two workgroups per CU, each segment keeping at least 4 listed blocks.
+  int64_t s = (2 * (int64_t)num_cus + rows - 1) / rows;
+  const int64_t by_len = x.top_k / 4 > 1 ? x.top_k / 4 : 1;
+  if (s > by_len) s = by_len;
+  if (s > VELOX_MAX_SPLITS) s = VELOX_MAX_SPLITS;
+  return (int32_t)(s < 1 ? 1 : s);
+}
+
+velox_status velox_sparse_attn_split(const velox_problem* p, const void* q, const void* k, const void* v,
+                                     const int32_t* kv_idx, const int32_t* kv_cnt, int32_t num_splits, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes, velox_stream_t stream) {
+  const velox_status st = check_problem(p, false);
+  if (st != VELOX_OK) return st;
+  if (num_splits < 1 || num_splits > VELOX_MAX_SPLITS) return VELOX_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !kv_idx || !kv_cnt || !out || !workspace) return VELOX_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VELOX_ERR_MISALIGNED;
+  const velox::Dims x = velox::dims(*p);
+  const int64_t parts = (int64_t)x.B * x.H * x.nq * num_splits;
+  if (parts > INT32_MAX / 2) return VELOX_ERR_UNSUPPORTED;
+  if (workspace_bytes < velox_sparse_attn_split_workspace_bytes(p, num_splits) || ((uintptr_t)workspace & 255u))
+    return VELOX_ERR_WORKSPACE;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)parts * x.blk * x.d * sizeof(float)));
+  return hip_status(velox::launch_sparse_attn(*p, q, k, v, kv_idx, kv_cnt, out, lse, num_splits, part_o, part_lse,
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 

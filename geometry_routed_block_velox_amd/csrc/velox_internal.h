@@ -19,9 +19,11 @@ hipError_t launch_cached_score(const velox_problem& p, const float* kbar, int ca
                                float* scores, int nscore, hipStream_t s);
 hipError_t launch_modulate_select(const velox_problem& p, const float* scores, const float* overlap,
                                   const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
+// splits == 0: one workgroup per row, direct output.  splits > 0: split-KV with
+// float32 partials part_o [rows*splits, blk, d] and part_lse [rows*splits, blk].
 hipError_t launch_sparse_attn(const velox_problem& p, const void* q, const void* k, const void* v,
-                              const int32_t* kv_idx, const int32_t* kv_cnt, void* out, float* lse,
-                              hipStream_t s);
+                              const int32_t* kv_idx, const int32_t* kv_cnt, void* out, float* lse, int splits,
+                              float* part_o, float* part_lse, hipStream_t s);
 
 // Derived sizes of a validated problem.
 struct Dims {

@@ -189,6 +189,35 @@ velox_status velox_sparse_attn(const velox_problem *p, const void *q, const void
                                const int32_t *kv_idx, const int32_t *kv_cnt, void *out, float *lse,
                                velox_stream_t stream);
 
+/* Split-KV attention for problems with few rows (fewer rows than compute
+ * units leave most of the GPU idle: the Small workload has 64 rows for 256
+ * CUs).  Each row's block list is cut into num_splits contiguous segments,
+ * list positions [s*cnt/num_splits, (s+1)*cnt/num_splits) for s = 0..num_splits-1;
+ * every segment is attended by its own workgroup, which writes a float32
+ * partial result (its normalised output and natural-log LSE) to the
+ * workspace, and a merge launch combines them exactly:
+ *   LSE = log sum_s exp(LSE_s),  out = sum_s exp(LSE_s - LSE) * out_s,
+ * segments without a valid block having weight 0.  Arguments and results
+ * are those of velox_sparse_attn (same kernels per segment; rounding may
+ * differ from the unsplit call in the last bits), plus:
+ *   num_splits   1 .. VELOX_MAX_SPLITS (else VELOX_ERR_BAD_SHAPE)
+ *   workspace    device scratch, 256-byte aligned, of at least
+ *                velox_sparse_attn_split_workspace_bytes(p, num_splits) bytes
+ *                (else VELOX_ERR_WORKSPACE).  Same article section as
+ *                velox_sparse_attn; the split itself is this library's
+ *                scheduling choice, not the article's. */
+#define VELOX_MAX_SPLITS 64
+size_t velox_sparse_attn_split_workspace_bytes(const velox_problem *p, int32_t num_splits);
+
+/* Host-only heuristic: a split count that gives about two workgroups per
+ * compute unit (num_cus, e.g. 256 on MI355X) with at least 4 listed blocks
+ * per segment; 1 when the rows alone fill the GPU or p is invalid. */
+int32_t velox_sparse_attn_auto_splits(const velox_problem *p, int32_t num_cus);
+
+velox_status velox_sparse_attn_split(const velox_problem *p, const void *q, const void *k, const void *v,
+                                     const int32_t *kv_idx, const int32_t *kv_cnt, int32_t num_splits, void *out,
+                                     float *lse, void *workspace, size_t workspace_bytes, velox_stream_t stream);
+
 /* Static English description of a status code. */
 const char *velox_status_string(velox_status s);
 

@@ -21,7 +21,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
-            "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached"} <= set(names)
+            "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached", "velox_sparse_attn_split",
+            "velox_sparse_attn_split_workspace_bytes", "velox_sparse_attn_auto_splits"} <= set(names)
     lib = C.CDLL(velox.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -140,6 +141,31 @@ def test_modulation_mode_is_validated():
     fake = C.c_void_p(0x100000)
     assert velox.lib().velox_sparse_attn(C.byref(p), fake, fake, fake, fake, fake, fake, None,
                                          None) == Status.BAD_SHAPE
+
+
+def test_split_entry_points_validate_before_launch():
+    L = velox.lib()
+    p = headline()
+    fake = C.c_void_p(0x100000)
+    assert L.velox_sparse_attn_split_workspace_bytes(C.byref(p), 0) == 0
+    assert L.velox_sparse_attn_split_workspace_bytes(C.byref(p), 65) == 0
+    need = L.velox_sparse_attn_split_workspace_bytes(C.byref(p), 4)
+    parts = 768 * 4
+    assert need == (parts * 128 * 128 * 4 + 255) // 256 * 256 + (parts * 128 * 4 + 255) // 256 * 256
+    call = lambda n, ws, wb: L.velox_sparse_attn_split(C.byref(p), fake, fake, fake, fake, fake, n, fake, None, ws,
+                                                       wb, None)
+    assert call(0, fake, need) == Status.BAD_SHAPE
+    assert call(65, fake, need) == Status.BAD_SHAPE
+    assert call(4, None, need) == Status.NULL_POINTER
+    assert call(4, fake, need - 1) == Status.WORKSPACE
+    assert call(4, C.c_void_p(0x100040), need) == Status.WORKSPACE
+    # auto splits: rows (768) fill 256 CUs -> 1; Small-like 64 rows -> 8 (two per CU), capped by list length
+    assert L.velox_sparse_attn_auto_splits(C.byref(p), 256) == 1
+    small = Problem(1, 4, 64, 1024, 12, 64, 48, 2.0, velox.VELOX_BF16)
+    assert L.velox_sparse_attn_auto_splits(C.byref(small), 256) == 8
+    tiny = Problem(1, 1, 64, 256, 8, 64, 12, 1.0, velox.VELOX_F32)
+    assert L.velox_sparse_attn_auto_splits(C.byref(tiny), 256) == 3
+    assert L.velox_last_hip_error() == 0
 
 
 def test_status_strings():
