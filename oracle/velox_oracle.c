@@ -217,6 +217,51 @@ int velox_oracle_modulate_logprob_f32(const float *s, const float *overlap, cons
   return 0;
 }
 
+/* Frustum-slice overlap (the article, Deep analysis, first and third steps:
+ * each past chunk is a camera frustum slice with a depth interval; the
+ * router asks which past slices overlap the region being drawn).  The
+ * article gives no geometry; the reading used here: chunk c sees the
+ * horizontal angles yaw_c +- fov/2 and depths [near_c, far_c]; query block
+ * i is the i-th of nq equal angular strips of the current view (yaw_C) with
+ * depths [qnear_i, qfar_i]; the overlap is the covered fraction of the
+ * strip's angle times the covered fraction of its depth interval:
+ *   O[b,i,c] = |strip_i ∩ (rel_c +- fov/2)| / |strip_i| *
+ *              |[qnear_i, qfar_i] ∩ [near_c, far_c]| / max(qfar_i - qnear_i, 1e-12)
+ * with rel_c = yaw_c - yaw_C wrapped to (-180, 180] and strip_i =
+ * [-fov/2 + fov*i/nq, -fov/2 + fov*(i+1)/nq]; covered[b,i] = (O[b,i,c] > 0
+ * for some c).  Inputs: yaw [B, C+1], past_depth [B, C, 2], query_depth
+ * [B, nq, 2] (float32, widened exactly); fp64 throughout. */
+int velox_oracle_frustum_overlap(const float *yaw, const float *past_depth, const float *query_depth, double fov,
+                                 int B, int nq, int C, double *overlap, uint8_t *covered) {
+  if (!yaw || !query_depth || !covered || (C > 0 && (!past_depth || !overlap)) || B < 0 || nq < 1 || C < 0 ||
+      !(fov > 0.0))
+    return -1;
+  const double half = fov / 2.0;
+  for (int b = 0; b < B; ++b) {
+    const double ycur = yaw[(int64_t)b * (C + 1) + C];
+    for (int i = 0; i < nq; ++i) {
+      const double s0 = -half + fov * i / nq, s1 = -half + fov * (i + 1) / nq;
+      const double q0 = query_depth[((int64_t)b * nq + i) * 2], q1 = query_depth[((int64_t)b * nq + i) * 2 + 1];
+      const double qlen = fmax(q1 - q0, 1e-12);
+      int any = 0;
+      for (int c = 0; c < C; ++c) {
+        double rel = fmod((double)yaw[(int64_t)b * (C + 1) + c] - ycur + 180.0, 360.0);
+        if (rel < 0.0) rel += 360.0;
+        rel -= 180.0;
+        if (rel == -180.0) rel = 180.0;
+        const double ang = fmax(0.0, fmin(s1, rel + half) - fmax(s0, rel - half)) / (s1 - s0);
+        const double n0 = past_depth[((int64_t)b * C + c) * 2], n1 = past_depth[((int64_t)b * C + c) * 2 + 1];
+        const double dep = fmax(0.0, fmin(q1, n1) - fmax(q0, n0)) / qlen;
+        const double o = ang * dep;
+        overlap[((int64_t)b * nq + i) * C + c] = o;
+        any |= o > 0.0;
+      }
+      covered[(int64_t)b * nq + i] = (uint8_t)any;
+    }
+  }
+  return 0;
+}
+
 typedef struct {
   double m;
   int j;

@@ -35,6 +35,7 @@ def lib():
         L.velox_oracle_scores.argtypes = [_P, _P, _L, _I, _I, _I, _P]
         L.velox_oracle_modulate.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _P]
         L.velox_oracle_modulate_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]
+        L.velox_oracle_frustum_overlap.argtypes = [_P, _P, _P, _D, _I, _I, _I, _P, _P]
         L.velox_oracle_modulate_logprob.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _P]
         L.velox_oracle_modulate_logprob_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]
         L.velox_oracle_select.argtypes = [_P, _L, _I, _I, _P, _P, _P]
@@ -115,6 +116,22 @@ def modulate(s: np.ndarray, overlap: np.ndarray, covered: np.ndarray, blk: int, 
         rc = fn(_ptr(s64), _ptr(ov), _ptr(cov), B, H, nq, nk, blk, T, C_, float(alpha), _ptr(m))
     _check(rc, "modulate")
     return m
+
+
+def frustum_overlap(yaw: np.ndarray, past_depth: np.ndarray, query_depth: np.ndarray, fov: float):
+    """Overlap [B,nq,C] (fp64) and covered [B,nq] (uint8) of frustum slices: yaw [B,C+1],
+    past_depth [B,C,2], query_depth [B,nq,2] (float32; see velox_oracle_frustum_overlap)."""
+    yaw = np.ascontiguousarray(yaw, np.float32)
+    pd = np.ascontiguousarray(past_depth, np.float32)
+    qd = np.ascontiguousarray(query_depth, np.float32)
+    B, C1 = yaw.shape
+    nq = qd.shape[1]
+    C = C1 - 1
+    o = np.empty((B, nq, C), np.float64)
+    cov = np.empty((B, nq), np.uint8)
+    _check(lib().velox_oracle_frustum_overlap(_ptr(yaw), _ptr(pd), _ptr(qd), float(fov), B, nq, C, _ptr(o),
+                                              _ptr(cov)), "frustum_overlap")
+    return o, cov
 
 
 def select(m: np.ndarray, k: int):

@@ -65,6 +65,7 @@ class Inputs:
     v: np.ndarray        # [B,H,N,d]
     overlap: np.ndarray  # [B,nq,C] float32
     covered: np.ndarray  # [B,nq] uint8
+    geometry: Optional[list] = None  # per batch element FrustumGeometry (frustum workloads)
 
     def as_f32(self, name: str) -> np.ndarray:
         a = getattr(self, name)
@@ -81,15 +82,33 @@ def _interval_overlap(a0, a1, b0, b1):
     return np.clip(np.minimum(a1, b1) - np.maximum(a0, b0), 0.0, None)
 
 
-def frustum_overlap(rng: np.random.Generator, nq: int, C: int) -> np.ndarray:
-    """Overlap [nq, C] between the current view's angular strips and past chunks' frusta."""
+@dataclass
+class FrustumGeometry:
+    """Synthetic camera geometry of one rollout (float32, as handed to a device)."""
+    yaw: np.ndarray          # [C+1] degrees; yaw[C] is the current view
+    past_depth: np.ndarray   # [C, 2] (near, far) metres of each past chunk's slice
+    query_depth: np.ndarray  # [nq, 2] (near, far) metres of each query block's strip
+    fov: float = FOV_DEG     # horizontal field of view in degrees
+
+
+def draw_frustum_geometry(rng: np.random.Generator, nq: int, C: int) -> FrustumGeometry:
     steps = rng.normal(0.0, YAW_STEP_STD_DEG, size=C) if C > 0 else np.zeros(0)
     yaw = np.concatenate([[0.0], np.cumsum(steps)])          # yaw[c], c = 0..C; yaw[C] = current view
     past_depth = np.sort(rng.uniform(*DEPTH_RANGE_M, size=(C, 2)), axis=1)
     q_depth = np.sort(rng.uniform(*DEPTH_RANGE_M, size=(nq, 2)), axis=1)
-    half = FOV_DEG / 2.0
+    return FrustumGeometry(yaw.astype(np.float32), past_depth.astype(np.float32), q_depth.astype(np.float32))
+
+
+def frustum_overlap(g: FrustumGeometry) -> np.ndarray:
+    """Overlap [nq, C] between the current view's angular strips and past chunks' frusta
+    (the workload's overlap input, evaluated in float64 from the float32 geometry)."""
+    yaw = g.yaw.astype(np.float64)
+    past_depth = g.past_depth.astype(np.float64)
+    q_depth = g.query_depth.astype(np.float64)
+    C, nq = past_depth.shape[0], q_depth.shape[0]
+    half = g.fov / 2.0
     # strips of the current view, in angles relative to the current yaw
-    edges = -half + FOV_DEG * np.arange(nq + 1) / nq
+    edges = -half + g.fov * np.arange(nq + 1) / nq
     s0, s1 = edges[:-1, None], edges[1:, None]                  # [nq,1]
     rel = _wrap_deg(yaw[:C] - yaw[C])[None, :]                  # [1,C]
     ang = _interval_overlap(s0, s1, rel - half, rel + half) / (s1 - s0)
@@ -108,14 +127,15 @@ def _draw_overlap(cfg: Config, rng: np.random.Generator):
         o = rng.beta(2.0, 5.0, size=(nq, C)).astype(np.float32)
         cov = np.ones(nq, dtype=np.uint8)
     elif cfg.overlap == "frustum":
-        o = frustum_overlap(rng, nq, C)
+        geom = draw_frustum_geometry(rng, nq, C)
+        o = frustum_overlap(geom)
         cov = (o > 0).any(axis=1).astype(np.uint8) if C > 0 else np.zeros(nq, np.uint8)
     else:
         raise ValueError(f"unknown overlap kind {cfg.overlap!r}")
     n_unc = int(round(cfg.uncovered_frac * nq))
     if n_unc > 0:
         cov[rng.choice(nq, n_unc, replace=False)] = 0
-    return o, cov
+    return o, cov, (geom if cfg.overlap == "frustum" else None)
 
 
 def _draw_head(cfg: Config, seed: int, h: int):
@@ -152,8 +172,9 @@ def make_inputs(cfg: Config, seeds: Optional[tuple] = None, threads: Optional[in
     v = np.empty((B, H, N, d), et)
     overlap = np.empty((B, cfg.nq, cfg.past_chunks), np.float32)
     covered = np.empty((B, cfg.nq), np.uint8)
+    geoms = [None] * B
     for b, seed in enumerate(seeds):
-        overlap[b], covered[b] = _draw_overlap(cfg, np.random.Generator(np.random.PCG64(seed)))
+        overlap[b], covered[b], geoms[b] = _draw_overlap(cfg, np.random.Generator(np.random.PCG64(seed)))
 
     def fill(job):
         b, h = job
@@ -167,4 +188,4 @@ def make_inputs(cfg: Config, seeds: Optional[tuple] = None, threads: Optional[in
     else:
         with ThreadPoolExecutor(nthreads) as ex:
             list(ex.map(fill, jobs))
-    return Inputs(cfg, q, k, v, overlap, covered)
+    return Inputs(cfg, q, k, v, overlap, covered, geoms if cfg.overlap == "frustum" else None)

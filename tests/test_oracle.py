@@ -273,6 +273,66 @@ def test_sign_safe_raising_overlap_never_drops_a_block():
     assert checked_negative > 10
 
 
+# ---------------------------------------------------------------- frustum-slice overlap
+
+def _geom(yaws, past, qdep):
+    return (np.asarray([yaws], np.float32), np.asarray([past], np.float32).reshape(1, -1, 2),
+            np.asarray([qdep], np.float32).reshape(1, -1, 2))
+
+
+def test_frustum_overlap_closed_forms():
+    # same view and same depth interval: every strip fully covered
+    o, cov = O.frustum_overlap(*_geom([0.0, 0.0], [[2.0, 9.0]], [[2.0, 9.0]] * 4), 90.0)
+    assert np.array_equal(o, np.ones((1, 4, 1))) and cov.all()
+    # turned by exactly one field of view: the slices only touch, overlap 0, uncovered
+    o, cov = O.frustum_overlap(*_geom([90.0, 0.0], [[2.0, 9.0]], [[2.0, 9.0]] * 2), 90.0)
+    assert np.all(o == 0) and not cov.any()
+    # turned by half a field of view: the right strip is covered, the left one is not
+    o, _ = O.frustum_overlap(*_geom([45.0, 0.0], [[2.0, 9.0]], [[2.0, 9.0]] * 2), 90.0)
+    assert list(o[0, :, 0]) == [0.0, 1.0]
+    # depth fractions: query [2,4] against [3,10] -> 1/2, [5,6] -> 0, [0,100] -> 1
+    o, _ = O.frustum_overlap(*_geom([0.0, 0.0, 0.0, 0.0], [[3.0, 10.0], [5.0, 6.0], [0.0, 100.0]], [[2.0, 4.0]]),
+                             90.0)
+    assert list(o[0, 0]) == [0.5, 0.0, 1.0]
+    # angle wrap: yaw 350 against a current yaw of 10 is 20 degrees to the left: strip [-45,45] vs [-65,25]
+    o, _ = O.frustum_overlap(*_geom([350.0, 10.0], [[1.0, 5.0]], [[1.0, 5.0]]), 90.0)
+    assert abs(o[0, 0, 0] - 70.0 / 90.0) < 1e-15
+    # no past chunk: nothing is covered
+    o, cov = O.frustum_overlap(np.zeros((1, 1), np.float32), np.zeros((1, 0, 2), np.float32),
+                               np.asarray([[[1.0, 2.0]] * 3], np.float32), 90.0)
+    assert o.shape == (1, 3, 0) and not cov.any()
+
+
+def test_frustum_overlap_is_the_covered_measure_monte_carlo():
+    """O is the fraction of the strip x depth box (uniform measure) inside the chunk's
+    angular and depth intervals: estimate it by sampling and compare within 5 sigma."""
+    rng = np.random.default_rng(31)
+    nq, C, fov, n = 5, 6, 90.0, 200000
+    yaw = np.concatenate([rng.uniform(-200, 200, C), [rng.uniform(-30, 30)]]).astype(np.float32)
+    past = np.sort(rng.uniform(1, 20, (C, 2)), axis=1).astype(np.float32)
+    qdep = np.sort(rng.uniform(1, 20, (nq, 2)), axis=1).astype(np.float32)
+    o, _ = O.frustum_overlap(yaw[None], past[None], qdep[None], fov)
+    for i in range(nq):
+        a = -fov / 2 + fov * (i + rng.random(n)) / nq               # angle relative to the current view
+        dep = qdep[i, 0] + (qdep[i, 1] - qdep[i, 0]) * rng.random(n)
+        for c in range(C):
+            diff = (a - (yaw[c] - yaw[C]) + 180.0) % 360.0 - 180.0  # angle relative to chunk c, wrapped
+            inside = (np.abs(diff) <= fov / 2) & (dep >= past[c, 0]) & (dep <= past[c, 1])
+            est = inside.mean()
+            sigma = math.sqrt(max(est * (1 - est), 1.0 / n) / n)
+            assert abs(est - o[0, i, c]) <= 5 * sigma + 1e-9, (i, c, est, o[0, i, c])
+
+
+def test_workload_overlap_equals_oracle_overlap():
+    from synth import draw_frustum_geometry, frustum_overlap
+    for seed in (3, 4, 5):
+        g = draw_frustum_geometry(np.random.default_rng(seed), 32, 48)
+        o, cov = O.frustum_overlap(g.yaw[None], g.past_depth[None], g.query_depth[None], g.fov)
+        w = frustum_overlap(g)
+        assert np.allclose(w, o[0], rtol=0, atol=1e-6)
+        assert np.array_equal((w > 0).any(axis=1), cov[0].astype(bool))
+
+
 # ---------------------------------------------------------------- attention
 
 def test_two_key_closed_form():
