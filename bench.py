@@ -189,6 +189,8 @@ def main():
                                    "attention_speedup_vs_keep_all": round(keep_all_ms / attn_avg, 3),
                                    "layer_speedup_vs_keep_all": round(keep_all_ms / ms_step, 3)}
 
+    if x.geometry is not None:
+        res["overlap_builder"] = bench_overlap_builder(velox, cfg, x, q, k, ws, stream)
     res["route_log_prob"] = bench_route_log_prob(velox, cfg, q, k, ov, cov, kv_idx, ws, stream)
     res["route_cached"] = bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el,
                                              x.overlap.nbytes + x.covered.nbytes + gi.nbytes + cnt.nbytes)
@@ -198,6 +200,59 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def bench_overlap_builder(velox, cfg, x, q, k, ws, stream, reps=20):
+    """The frustum-overlap builder alone, and the routing phase with the builder run
+    (a) after the scoring on the same stream and (b) on a side stream next to it,
+    joined by an event before the selection."""
+    import numpy as np
+    import torch
+    g = x.geometry
+    yaw = torch.from_numpy(np.stack([e.yaw for e in g])).cuda()
+    pd = torch.from_numpy(np.stack([e.past_depth for e in g])).cuda()
+    qd = torch.from_numpy(np.stack([e.query_depth for e in g])).cuda()
+    fov = g[0].fov
+    B, H, nq, nk = cfg.batch, cfg.heads, cfg.nq, cfg.nk
+    ov = torch.empty((B, nq, cfg.past_chunks), dtype=torch.float32, device="cuda")
+    cov = torch.empty((B, nq), dtype=torch.uint8, device="cuda")
+    s = torch.empty((B, H, nq, nk), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, H, nq, cfg.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, H, nq), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+
+    def sequential():
+        velox.score(q, k, cfg.block, scores=s, workspace=ws, stream=stream)
+        velox.frustum_overlap(yaw, pd, qd, fov, out=(ov, cov), stream=stream)
+        velox.select(s, ov, cov, cfg.block, cfg.top_k, cfg.alpha, stream=stream)
+
+    def concurrent():
+        side.wait_stream(stream)
+        velox.frustum_overlap(yaw, pd, qd, fov, out=(ov, cov), stream=side)
+        ready.record(side)
+        velox.score(q, k, cfg.block, scores=s, workspace=ws, stream=stream)
+        stream.wait_event(ready)
+        velox.select(s, ov, cov, cfg.block, cfg.top_k, cfg.alpha, stream=stream)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_builder = timed(lambda: velox.frustum_overlap(yaw, pd, qd, fov, out=(ov, cov), stream=stream))
+    t_seq, t_conc = timed(sequential), timed(concurrent)
+    return {"builder_ms": round(t_builder, 4), "route_with_builder_same_stream_ms": round(t_seq, 4),
+            "route_with_builder_side_stream_ms": round(t_conc, 4),
+            "note": "score -> select with the overlap built from the synthetic frustum geometry on the GPU; "
+                    "side stream = built concurrently with the scoring, joined by an event"}
 
 
 def bench_split_small(velox, stream, reps=50):

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   velox_check(problem) -> status
   velox_route_workspace_bytes(problem) -> int
   route(q, k, overlap, covered, block, top_k, alpha, ...) -> (kv_idx, kv_cnt[, scores])
+  score(q, k, block, ...) -> scores
+  frustum_overlap(yaw, past_depth, query_depth, fov_deg) -> (overlap, covered)
   pool_keys(k, chunk_tokens, block, first_block, num_blocks, ...) -> kbar cache
   route_cached(q, kbar, past_chunks, overlap, covered, block, top_k, alpha, ...) -> as route
   select(scores, overlap, covered, block, top_k, alpha) -> (kv_idx, kv_cnt)
@@ -23,7 +25,8 @@ from dataclasses import dataclass
 
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
-    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits",
+    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits", "score",
+    "frustum_overlap",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +88,10 @@ def lib():
         L.velox_route_workspace_bytes.restype = C.c_size_t
         L.velox_route.argtypes = [P, V, V, V, V, V, V, V, V, C.c_size_t, V]
         L.velox_route.restype = C.c_int
+        L.velox_score.argtypes = [P, V, V, V, V, C.c_size_t, V]
+        L.velox_score.restype = C.c_int
+        L.velox_frustum_overlap.argtypes = [P, V, V, V, C.c_float, V, V, V]
+        L.velox_frustum_overlap.restype = C.c_int
         L.velox_pool_keys.argtypes = [P, V, V, C.c_int32, C.c_int32, C.c_int32, V]
         L.velox_pool_keys.restype = C.c_int
         L.velox_route_cached.argtypes = [P, V, V, C.c_int32, V, V, V, V, V, V, C.c_size_t, V]
@@ -207,6 +214,56 @@ def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_s
                            _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "velox_route")
     return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
+
+
+def score(q, k, block: int, scores=None, workspace=None, stream=None):
+    """velox_score: raw importance s [B,H,nq,nk] float32 (the scoring step of route)."""
+    torch = _torch()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, ndim=4)
+    B, H, T, d = q.shape
+    p = problem_for(tuple(q.shape), k.shape[2], block, T // block, 0.0, _dtype_code(q))
+    _raise(velox_check(p), "velox_score")
+    if scores is None:
+        scores = torch.empty((B, H, p.nq, p.nk), dtype=torch.float32, device=q.device)
+    _dev(scores, "scores", torch.float32, ndim=4)
+    if tuple(scores.shape) != (B, H, p.nq, p.nk):
+        raise ValueError(f"scores must be [{B},{H},{p.nq},{p.nk}]")
+    need = velox_route_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _raise(lib().velox_score(C.byref(p), _ptr(q), _ptr(k), _ptr(scores), _ptr(workspace), workspace.numel(),
+                             _stream(stream)), "velox_score")
+    return scores
+
+
+def frustum_overlap(yaw, past_depth, query_depth, fov_deg: float, out=None, stream=None):
+    """velox_frustum_overlap: yaw [B,C+1], past_depth [B,C,2], query_depth [B,nq,2] (float32, GPU)
+    -> (overlap [B,nq,C] float32, covered [B,nq] uint8)."""
+    torch = _torch()
+    _dev(yaw, "yaw", torch.float32, ndim=2)
+    _dev(query_depth, "query_depth", torch.float32, ndim=3)
+    B, C1 = yaw.shape
+    nq = query_depth.shape[1]
+    C_ = C1 - 1
+    if tuple(query_depth.shape) != (B, nq, 2):
+        raise ValueError("query_depth must be [B,nq,2]")
+    if C_ > 0:
+        _dev(past_depth, "past_depth", torch.float32, ndim=3)
+        if tuple(past_depth.shape) != (B, C_, 2):
+            raise ValueError("past_depth must be [B,C,2]")
+    # the problem only carries the shapes: nq query blocks of 64 tokens, C past chunks
+    p = Problem(B, 1, 64, nq * 64, C_, 64, nq, 0.0, VELOX_F32)
+    if out is None:
+        overlap = torch.empty((B, nq, C_), dtype=torch.float32, device=yaw.device)
+        covered = torch.empty((B, nq), dtype=torch.uint8, device=yaw.device)
+    else:
+        overlap, covered = out
+    st = lib().velox_frustum_overlap(C.byref(p), _ptr(yaw), _ptr(past_depth if C_ > 0 else None),
+                                     _ptr(query_depth), float(fov_deg), _ptr(overlap if C_ > 0 else None),
+                                     _ptr(covered), _stream(stream))
+    _raise(st, "velox_frustum_overlap")
+    return overlap, covered
 
 
 def pool_keys(k, chunk_tokens: int, block: int, first_block: int, num_blocks: int, kbar=None,

@@ -77,6 +77,33 @@ velox_status velox_route(const velox_problem* p, const void* q, const void* k, c
   return hip_status(e);
 }
 
+velox_status velox_score(const velox_problem* p, const void* q, const void* k, float* scores, void* workspace,
+                         size_t workspace_bytes, velox_stream_t stream) {
+  const velox_status st = velox_check(p);
+  if (st != VELOX_OK) return st;
+  if (!q || !k || !scores || !workspace) return VELOX_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k)) return VELOX_ERR_MISALIGNED;
+  if (workspace_bytes < velox_route_workspace_bytes(p) || ((uintptr_t)workspace & 255u))
+    return VELOX_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float* qbar = static_cast<float*>(workspace);
+  hipError_t e = velox::launch_pool_queries(*p, q, qbar, hs);
+  if (e == hipSuccess) e = velox::launch_block_score(*p, k, qbar, scores, hs);
+  return hip_status(e);
+}
+
+velox_status velox_frustum_overlap(const velox_problem* p, const float* yaw, const float* past_depth,
+                                   const float* query_depth, float fov_deg, float* overlap, uint8_t* covered,
+                                   velox_stream_t stream) {
+  const velox_status st = check_problem(p, false);
+  if (st != VELOX_OK) return st;
+  if (!yaw || !query_depth || !covered || (p->past_chunks > 0 && (!past_depth || !overlap)))
+    return VELOX_ERR_NULL_POINTER;
+  if (!(fov_deg > 0.f && fov_deg <= 180.f)) return VELOX_ERR_BAD_SHAPE;
+  return hip_status(velox::launch_frustum_overlap(*p, yaw, past_depth, query_depth, fov_deg, overlap, covered,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 velox_status velox_pool_keys(const velox_problem* p, const void* k, float* kbar, int32_t cache_blocks,
                              int32_t first_block, int32_t num_blocks, velox_stream_t stream) {
   const velox_status st = check_problem(p, false);

@@ -130,6 +130,37 @@ velox_status velox_route(const velox_problem *p, const void *q, const void *k, c
                          const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, float *scores,
                          void *workspace, size_t workspace_bytes, velox_stream_t stream);
 
+/* The scoring step of velox_route alone: writes the raw importance
+ * s [B,H,nq,nk] float32 (same values as velox_route's `scores`) for a later
+ * velox_select.  Lets a caller build the overlap concurrently (below) and
+ * join before the selection.  workspace: at least
+ * velox_route_workspace_bytes(p) bytes, 256-byte aligned. */
+velox_status velox_score(const velox_problem *p, const void *q, const void *k, float *scores, void *workspace,
+                         size_t workspace_bytes, velox_stream_t stream);
+
+/* Overlap of past chunks' camera-frustum slices with the current view's
+ * query strips (the article's Deep analysis, first and third steps; the
+ * slices are built asynchronously next to denoising, same section).  The
+ * article gives no geometry; here chunk c sees horizontal angles
+ * yaw_c +- fov/2 and depths [near_c, far_c], query block i is the i-th of nq
+ * equal angular strips of the current view (yaw_C) with depths
+ * [qnear_i, qfar_i], and
+ *   overlap[b,i,c] = (fraction of strip i's angle inside chunk c's range)
+ *                  * (fraction of [qnear_i, qfar_i] inside [near_c, far_c])
+ * with angle differences wrapped to (-180, 180]; covered[b,i] = 1 if any
+ * overlap of the row is > 0, else 0.  float32 arithmetic.
+ *   yaw          [B, C+1] float32 degrees, yaw[b, C] = the current view
+ *   past_depth   [B, C, 2] float32 (near, far) of each past chunk
+ *   query_depth  [B, nq, 2] float32 (near, far) of each query strip
+ *   fov_deg      horizontal field of view, in (0, 180] (else VELOX_ERR_BAD_SHAPE)
+ *   overlap      [B, nq, C] float32 out (may be NULL when C == 0)
+ *   covered      [B, nq] uint8 out
+ * Only batch, chunk_tokens, block and past_chunks of p are used (the rest
+ * must be valid). */
+velox_status velox_frustum_overlap(const velox_problem *p, const float *yaw, const float *past_depth,
+                                   const float *query_depth, float fov_deg, float *overlap, uint8_t *covered,
+                                   velox_stream_t stream);
+
 /* Incremental pooled-key cache (the article's Outlook section: behaviour for
  * rollouts far longer than 48 chunks; with the cache kept per layer, past
  * chunks' keys, which do not change, are pooled once instead of on every

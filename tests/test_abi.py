@@ -22,7 +22,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
             "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached", "velox_sparse_attn_split",
-            "velox_sparse_attn_split_workspace_bytes", "velox_sparse_attn_auto_splits"} <= set(names)
+            "velox_sparse_attn_split_workspace_bytes", "velox_sparse_attn_auto_splits", "velox_score",
+            "velox_frustum_overlap"} <= set(names)
     lib = C.CDLL(velox.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -165,6 +166,21 @@ def test_split_entry_points_validate_before_launch():
     assert L.velox_sparse_attn_auto_splits(C.byref(small), 256) == 8
     tiny = Problem(1, 1, 64, 256, 8, 64, 12, 1.0, velox.VELOX_F32)
     assert L.velox_sparse_attn_auto_splits(C.byref(tiny), 256) == 3
+    assert L.velox_last_hip_error() == 0
+
+
+def test_score_and_overlap_builder_validate_before_launch():
+    L = velox.lib()
+    p = headline()
+    fake = C.c_void_p(0x100000)
+    ws = velox.velox_route_workspace_bytes(p)
+    assert L.velox_score(C.byref(p), fake, fake, None, fake, ws, None) == Status.NULL_POINTER
+    assert L.velox_score(C.byref(p), fake, fake, fake, fake, ws - 1, None) == Status.WORKSPACE
+    assert L.velox_score(C.byref(p), C.c_void_p(0x100002), fake, fake, fake, ws, None) == Status.MISALIGNED
+    for fov in (0.0, -5.0, 180.5, float("nan")):
+        assert L.velox_frustum_overlap(C.byref(p), fake, fake, fake, fov, fake, fake, None) == Status.BAD_SHAPE
+    assert L.velox_frustum_overlap(C.byref(p), fake, None, fake, 90.0, fake, fake, None) == Status.NULL_POINTER
+    assert L.velox_frustum_overlap(C.byref(p), fake, fake, fake, 90.0, None, fake, None) == Status.NULL_POINTER
     assert L.velox_last_hip_error() == 0
 
 
