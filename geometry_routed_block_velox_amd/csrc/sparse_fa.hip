@@ -8,11 +8,15 @@
 // computed with an online softmax over the list, one KV block (= one tile)
 // at a time.  No causal mask.
 //
-// bf16 kernel (sparse_fa_bf16_kernel): one workgroup of 4 waves per row.
-//  * Work split: wave w owns query half w&1 and key half w>>1 of every tile
-//    (64 queries x 64 keys at blk = 128), so each K/V operand fragment read
-//    from LDS feeds two MFMAs.  The two key halves keep independent online
-//    softmax states that are merged once at the end of the row.
+// bf16 kernel (sparse_fa_bf16_kernel): one workgroup per row, 2*blk/32 waves
+// (8 at blk = 128, i.e. two waves per SIMD).
+//  * Work split: wave w owns 32 queries (query group w % (blk/32)) and one key
+//    half (w / (blk/32)) of every tile: 32 queries x 64 keys at blk = 128.
+//    Two waves per SIMD let one wave's softmax and LDS waits overlap the
+//    other's MFMAs; the price is twice the LDS operand reads per MFMA of a
+//    64-query split (measured: the two-wave split is faster).  The two key
+//    halves keep independent online softmax states that are merged once at
+//    the end of the row.
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: lane l of an accumulator holds query l%32 and
 //    keys 8(r/4) + 4(l/32) + r%4, so softmax statistics need one lane
@@ -24,9 +28,10 @@
 //    four consecutive rows of column i -- exactly the accumulator's key order.
 //  * K and V tiles go from HBM straight to LDS (global_load_lds_dwordx4, no
 //    register staging), double-buffered so that the loads of the next listed
-//    block overlap the MFMA work on the current one; one barrier per block.  16-byte chunks are XOR-swizzled per row so
-//    that the MFMA operand reads of K and the transpose reads of V spread
-//    over the banks.
+//    block overlap the MFMA work on the current one; one barrier per block.
+//    16-byte chunks are XOR-swizzled per row so that the MFMA operand reads
+//    of K and the transpose reads of V spread over the banks.  K operand
+//    fragments are read two MFMA steps ahead of their use.
 //  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
 //    Each wave fixes its softmax reference maximum m_ref per query from the
 //    first listed block (the exact maximum over that block, so the largest
@@ -55,14 +60,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// d-steps by which the K fragment reads run ahead of their score MFMAs.
+constexpr int kKAhead = 2;
+
 // Per-block probability sum above which a row is recomputed at its true maximum.
 constexpr float kOverflowGuard = 1099511627776.0f;  // 2^40
 
 template <int D, int BLK>
 struct Fa {
-  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int QW = 32;                 // queries per wave
+  static constexpr int NQG = BLK / QW;          // query groups
+  static constexpr int NW = 2 * NQG;            // waves per workgroup: query groups x two key halves
   static constexpr int NT = NW * 64;
-  static constexpr int QW = BLK / 2;            // queries per wave
   static constexpr int KW = BLK / 2;            // keys per wave and tile
   static constexpr int QT = QW / 32;            // 32-query MFMA tiles per wave
   static constexpr int KTW = KW / 32;           // 32-key MFMA tiles per wave
@@ -177,16 +186,29 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][qt][r] = 0.f;
 
-#pragma unroll
-  for (int s = 0; s < F::DS; ++s) {
+  // K fragments are read kKAhead d-steps ahead of their MFMAs; the scheduling
+  // fences (which let vector ALU work move across) keep that order, so the
+  // LDS latency is covered by the MFMAs in between.
+  uint4 kf[F::DS][F::KTW];
+  auto kread = [&](int s) {
 #pragma unroll
     for (int kt = 0; kt < F::KTW; ++kt) {
       const int row = kbase + 32 * kt + qc;
-      const bf16x8 a = as_bf16x8(st[row * F::NCH + ((2 * s + hh) ^ F::swz_k(row))]);
+      kf[s][kt] = st[row * F::NCH + ((2 * s + hh) ^ F::swz_k(row))];
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kKAhead && s < F::DS; ++s) kread(s);
+#pragma unroll
+  for (int s = 0; s < F::DS; ++s) {
+    if (s + kKAhead < F::DS) kread(s + kKAhead);
+    __builtin_amdgcn_sched_barrier(0x406);
+#pragma unroll
+    for (int kt = 0; kt < F::KTW; ++kt)
 #pragma unroll
       for (int qt = 0; qt < F::QT; ++qt)
-        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
-    }
+        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s][kt]), w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0x406);
   }
 
   if constexpr (MODE != Mode::Normal) {
@@ -315,7 +337,7 @@ __device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* 
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
+__global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave & 1, kg = wave >> 1;
+  const int qg = wave % F::NQG, kg = wave / F::NQG;
   const int qc = lane & 31, hh = lane >> 5;
   const int kbase = kg * F::KW;
   const Segment sg = segment_of(xcd_grouped(blockIdx.x, gridDim.x), splits, kv_cnt, top_k);
@@ -387,7 +409,7 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) {
       xm[(qg * F::QT + qt) * 64 + lane] = w.m[qt];
-      xm[((2 + qg) * F::QT + qt) * 64 + lane] = lw[qt];
+      xm[((F::NQG + qg) * F::QT + qt) * 64 + lane] = lw[qt];
 #pragma unroll
       for (int dt = 0; dt < F::DT; ++dt)
 #pragma unroll
@@ -399,7 +421,7 @@ __global__ __launch_bounds__(256) void sparse_fa_bf16_kernel(
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) {
       const float m1 = xm[(qg * F::QT + qt) * 64 + lane];
-      const float l1 = xm[((2 + qg) * F::QT + qt) * 64 + lane];
+      const float l1 = xm[((F::NQG + qg) * F::QT + qt) * 64 + lane];
       const float m0 = w.m[qt];
       const float mm = fmaxf(m0, m1);
       const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * scale_log2);
