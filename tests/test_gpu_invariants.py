@@ -43,7 +43,7 @@ def run_layer(x, top_k=None, alpha=None, covered=None):
 
 
 # shapes spanning several tiles with ragged tails (nk not a multiple of the
-# 16-block scoring group), all four (d, blk) builds, both dtypes and B > 1
+# 32-block scoring group), all four (d, blk) builds, both dtypes and B > 1
 EDGE = [
     ("bf16-d128-b128-B2", dict(batch=2, heads=3, head_dim=128, chunk_tokens=384, past_chunks=6, block=128,
                                top_k=9, dtype="bf16", seeds=(21, 22))),
