@@ -540,40 +540,46 @@ __global__ __launch_bounds__(BLK) void sparse_fa_f32_kernel(const float* __restr
 // Combine the segments of every row: with L_s the segment LSEs and O_s their
 // normalised outputs, LSE = log sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s
 // (segments without a valid block have L_s = -inf and weight 0).  One thread
-// per output element; grid = ceil(rows * BLK * D / 256).
+// per output token and 4 consecutive d; grid = ceil(rows * BLK * D / 4 / 256).
 template <int D, int BLK, bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse, int splits,
-                                                           long long n_elem, void* __restrict__ out,
+                                                           long long n_vec, void* __restrict__ out,
                                                            float* __restrict__ lse) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n_elem) return;
-  const long long tok = e / D;  // = row * BLK + t, also the output token index
-  const int d = (int)(e % D);
+  if (e >= n_vec) return;
+  const long long tok = e / (D / 4);  // = row * BLK + t, also the output token index
+  const int d = (int)(e % (D / 4)) * 4;
   const long long row = tok / BLK;
   const int t = (int)(tok % BLK);
   const float* pl = part_lse + row * splits * BLK + t;
   float mx = -__builtin_inff();
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(size_t)s * BLK]);
-  float acc = 0.f, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
   if (mx > -__builtin_inff()) {
     const float* po = part_o + (row * splits * BLK + t) * D + d;
     for (int s = 0; s < splits; ++s) {
       const float ls = pl[(size_t)s * BLK];
       if (ls == -__builtin_inff()) continue;
       const float w = __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);
+      const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * BLK * D);
       wsum += w;
-      acc += w * po[(size_t)s * BLK * D];
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
     }
   }
-  const float o = wsum > 0.f ? acc / wsum : 0.f;
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (OUT_BF16) {
-    const __bf16 b = (__bf16)o;
-    uint16_t u;
-    __builtin_memcpy(&u, &b, 2);
-    static_cast<uint16_t*>(out)[e] = u;
+    uint2 pk;
+    pk.x = pack_bf16x2(o.x, o.y);
+    pk.y = pack_bf16x2(o.z, o.w);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + tok * D + d) = pk;
   } else {
-    static_cast<float*>(out)[e] = o;
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + tok * D + d) = o;
   }
   if (lse && d == 0) lse[tok] = wsum > 0.f ? mx + __builtin_logf(wsum) : -__builtin_inff();
 }
@@ -596,7 +602,7 @@ hipError_t fa_bf16(const Dims& x, const void* q, const void* k, const void* v, c
 template <int D, int BLK, bool OUT_BF16>
 hipError_t merge(const Dims& x, int splits, const float* part_o, const float* part_lse, void* out, float* lse,
                  hipStream_t s) {
-  const long long n = (long long)x.B * x.H * x.nq * BLK * D;
+  const long long n = (long long)x.B * x.H * x.nq * BLK * (D / 4);
   hipLaunchKernelGGL((merge_splits_kernel<D, BLK, OUT_BF16>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      part_o, part_lse, splits, n, out, lse);
   return hipGetLastError();
