@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
+    ap.add_argument("--cold-reps", type=int, default=10, help="layers timed after a 1 GiB cache-flushing write")
+    ap.add_argument("--no-probe", action="store_true", help="skip the MFMA-only peak probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counter scaling)")
     return ap.parse_args()
@@ -121,6 +123,19 @@ def main():
     layer_ms = [a.elapsed_time(c) for a, _, c in ev]
     ms_step = wall * 1e3 / args.steps
 
+    # cold protocol: a 1 GiB scratch write (4x the 256 MB MALL) before each timed layer
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold_ms = []
+    for _ in range(args.cold_reps):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(e0.elapsed_time(e1))
+    del scratch
+
     cnt = kv_cnt.cpu().numpy()
     f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
     f_dense = float(cfg.flops_dense())
@@ -153,6 +168,7 @@ def main():
             "global_batch": B, "seq_len": cfg.kv_tokens, "parallelism": "none (1 GPU)",
         },
         "ms_per_layer_events_median": round(float(np.median(layer_ms)), 4),
+        "ms_per_layer_cold_median": round(float(np.median(cold_ms)), 4) if cold_ms else None,
         "route_ms": round(route_avg, 4),
         "attn_ms": round(attn_avg, 4),
         "dense_equiv_tflops": round(f_dense / (ms_step * 1e-3) / 1e12, 2),
@@ -170,6 +186,11 @@ def main():
             "kv_union_blocks": union_blocks,
         },
     }
+
+    if not args.no_probe:
+        probe = bench_mfma_probe(velox, stream)
+        res["mfma_probe"] = probe
+        res["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / probe["tflops"], 4)
 
     if not args.no_context:
         # keep-all through the same kernel: the same-kernel "dense" comparison at this chunk
@@ -200,6 +221,27 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def bench_mfma_probe(velox, stream, grid=256, iters=20000):
+    """The MFMA-only kernel on every CU: the bf16 rate and shader clock this chip sustains."""
+    import numpy as np
+    import torch
+    velox.mfma_probe(grid, 100, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    clocks = velox.mfma_probe(grid, iters, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    c = clocks.cpu().numpy().astype(np.float64)
+    ghz = float(np.median(c[:, 0] / (c[:, 1] / 100e6)) / 1e9)
+    flops = grid * 4.0 * iters * 16 * 32768
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "sclk_ghz": round(ghz, 3), "grid": grid, "iters": iters,
+            "frac_of_published_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "v_mfma_f32_32x32x16_bf16 only, operands in registers; shader clock from s_memtime vs "
+                    "s_memrealtime inside the kernel"}
 
 
 def bench_overlap_builder(velox, cfg, x, q, k, ws, stream, reps=20):

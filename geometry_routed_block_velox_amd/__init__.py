@@ -26,7 +26,7 @@ from dataclasses import dataclass
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
     "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits", "score",
-    "frustum_overlap",
+    "frustum_overlap", "mfma_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +106,8 @@ def lib():
         L.velox_sparse_attn_auto_splits.restype = C.c_int32
         L.velox_sparse_attn_split.argtypes = [P, V, V, V, V, V, C.c_int32, V, V, V, C.c_size_t, V]
         L.velox_sparse_attn_split.restype = C.c_int
+        L.velox_mfma_probe.argtypes = [C.c_int32, C.c_int32, V, V, V]
+        L.velox_mfma_probe.restype = C.c_int
         L.velox_status_string.argtypes = [C.c_int]
         L.velox_status_string.restype = C.c_char_p
         L.velox_last_hip_error.argtypes = []
@@ -347,6 +349,16 @@ def select(scores, overlap, covered, block: int, top_k: int, alpha: float, strea
                             _stream(stream))
     _raise(st, "velox_select")
     return kv_idx, kv_cnt
+
+
+def mfma_probe(grid: int, iters: int, stream=None):
+    """velox_mfma_probe: launch the MFMA-only kernel; returns the device clock record
+    (int64 [grid, 2]: shader clocks, 100 MHz reference clocks).  FLOPs = grid*4*iters*16*32768."""
+    torch = _torch()
+    clocks = torch.zeros((grid, 2), dtype=torch.int64, device="cuda")
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    _raise(lib().velox_mfma_probe(int(grid), int(iters), _ptr(clocks), _ptr(sink), _stream(stream)), "velox_mfma_probe")
+    return clocks
 
 
 def auto_splits(p: Problem, num_cus: int | None = None) -> int:

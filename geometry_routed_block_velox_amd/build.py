@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvelox.so")
-SOURCES = ["velox_api.cpp", "block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip"]
+SOURCES = ["velox_api.cpp", "block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -206,6 +206,12 @@ velox_status velox_sparse_attn_split(const velox_problem* p, const void* q, cons
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
+velox_status velox_mfma_probe(int32_t grid, int32_t iters, int64_t* clocks, float* sink, velox_stream_t stream) {
+  if (!clocks || !sink) return VELOX_ERR_NULL_POINTER;
+  if (grid < 1 || grid > 65536 || iters < 1) return VELOX_ERR_BAD_SHAPE;
+  return hip_status(velox::launch_mfma_probe(grid, iters, clocks, sink, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* velox_status_string(velox_status s) {
   switch (s) {
     case VELOX_OK: return "ok";

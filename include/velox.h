@@ -249,6 +249,17 @@ velox_status velox_sparse_attn_split(const velox_problem *p, const void *q, cons
                                      const int32_t *kv_idx, const int32_t *kv_cnt, int32_t num_splits, void *out,
                                      float *lse, void *workspace, size_t workspace_bytes, velox_stream_t stream);
 
+/* Measurement aid (not part of the layer): an MFMA-only kernel of `grid`
+ * workgroups x 4 waves, each wave running iters x 16 independent
+ * v_mfma_f32_32x32x16_bf16 with register operands, so the caller can measure
+ * the bf16 matrix-core rate the chip sustains (FLOPs = grid*4*iters*16*32768,
+ * timed with events on `stream`) next to the published peak.  Writes, per
+ * workgroup, the elapsed shader clocks and elapsed 100 MHz reference clocks
+ * of its first wave to clocks[2*wg], clocks[2*wg+1] (device, int64), and one
+ * float per thread to sink (device, grid*256 floats).  1 <= grid <= 65536,
+ * iters >= 1 (else VELOX_ERR_BAD_SHAPE). */
+velox_status velox_mfma_probe(int32_t grid, int32_t iters, int64_t *clocks, float *sink, velox_stream_t stream);
+
 /* Static English description of a status code. */
 const char *velox_status_string(velox_status s);
 

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
             "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached", "velox_sparse_attn_split",
             "velox_sparse_attn_split_workspace_bytes", "velox_sparse_attn_auto_splits", "velox_score",
-            "velox_frustum_overlap"} <= set(names)
+            "velox_frustum_overlap", "velox_mfma_probe"} <= set(names)
     lib = C.CDLL(velox.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -182,6 +182,14 @@ def test_score_and_overlap_builder_validate_before_launch():
     assert L.velox_frustum_overlap(C.byref(p), fake, None, fake, 90.0, fake, fake, None) == Status.NULL_POINTER
     assert L.velox_frustum_overlap(C.byref(p), fake, fake, fake, 90.0, None, fake, None) == Status.NULL_POINTER
     assert L.velox_last_hip_error() == 0
+
+
+def test_mfma_probe_validates_before_launch():
+    L = velox.lib()
+    fake = C.c_void_p(0x100000)
+    assert L.velox_mfma_probe(0, 10, fake, fake, None) == Status.BAD_SHAPE
+    assert L.velox_mfma_probe(256, 0, fake, fake, None) == Status.BAD_SHAPE
+    assert L.velox_mfma_probe(256, 10, None, fake, None) == Status.NULL_POINTER
 
 
 def test_status_strings():
