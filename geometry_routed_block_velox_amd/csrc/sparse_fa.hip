@@ -31,7 +31,10 @@
 //    block overlap the MFMA work on the current one; one barrier per block.
 //    16-byte chunks are XOR-swizzled per row so that the MFMA operand reads
 //    of K and the transpose reads of V spread over the banks.  K operand
-//    fragments are read two MFMA steps ahead of their use.
+//    fragments are read two MFMA steps ahead of their use.  Every LDS operand
+//    address is a per-lane register computed once per workgroup plus an
+//    instruction immediate (stage, key tile, 16-key step): the block loop is
+//    unrolled over the two stages, so it does no address arithmetic.
 //  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
 //    Each wave fixes its softmax reference maximum m_ref per query from the
 //    first listed block (the exact maximum over that block, so the largest
@@ -82,6 +85,8 @@ struct Fa {
   static constexpr int TILE_CHUNKS = BLK * NCH; // per K (or V) tile
   static constexpr int SEGS_PER_WAVE = TILE_CHUNKS / 64 / NW;  // 1 KiB DMA segments
   static_assert(QT >= 1 && KTW >= 1 && NCH >= 8 && SEGS_PER_WAVE >= 1, "unsupported tile shape");
+  static constexpr int T = BLK * D * 2;             // bytes of one K (or V) tile
+  static constexpr int V0 = 2 * T, LDS_BYTES = 4 * T;  // K stages at 0 and T, V stages at 2T and 3T
   static __device__ __forceinline__ int swz_k(int row) { return row & (NCH - 1); }
   static __device__ __forceinline__ int swz_v(int row) { return (4 * row) & (NCH - 1); }
 };
@@ -141,20 +146,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-template <int D, int BLK>
-__device__ __forceinline__ void issue_tile(uint4* st, const uint16_t* __restrict__ kh,
+template <int ST, int D, int BLK>
+__device__ __forceinline__ void issue_tile(uint32_t lds0, const uint16_t* __restrict__ kh,
                                            const uint16_t* __restrict__ vh, int j, int wave,
                                            const DmaOffsets<D, BLK>& off) {
   using F = Fa<D, BLK>;
   const uint16_t* kb = kh + (size_t)j * BLK * D;
   const uint16_t* vb = vh + (size_t)j * BLK * D;
-  const uint32_t base = lds_addr(st);
 #pragma unroll
   for (int i = 0; i < F::SEGS_PER_WAVE; ++i) {
-    const uint32_t seg = (uint32_t)(wave * F::SEGS_PER_WAVE + i);
-    lds_dma16(base + seg * 1024u, kb, off.k[i]);
-    lds_dma16(base + F::TILE_CHUNKS * 16u + seg * 1024u, vb, off.v[i]);
+    const uint32_t seg = (uint32_t)(wave * F::SEGS_PER_WAVE + i) * 1024u;
+    lds_dma16(lds0 + ST * F::T + seg, kb, off.k[i]);
+    lds_dma16(lds0 + F::V0 + ST * F::T + seg, vb, off.v[i]);
   }
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  const u32x4 x = *(const lds_u32x4_t*)(uintptr_t)addr;
+  bf16x8 r;
+  __builtin_memcpy(&r, &x, 16);
+  return r;
 }
 
 // Per-wave state of the online softmax over this wave's key half.
@@ -166,6 +180,9 @@ struct WaveState {
   float m[F::QT];              // reference maximum (raw logits) of query qc of tile qt
   float l[F::QT];              // this lane's partial sum of probabilities
   bool bad;                    // a probability sum crossed kOverflowGuard
+  // Per-lane LDS byte addresses in stage 0; stage, key tile, step and half are immediate offsets.
+  uint32_t ko[F::DS];          // K fragment of d-step s, key tile 0
+  uint32_t vo[F::DT];          // first V^T transpose read of d tile dt
 };
 
 enum class Mode { First, Normal, MaxOnly };
@@ -174,9 +191,8 @@ enum class Mode { First, Normal, MaxOnly };
 //   Mode::First   m_ref = maximum of this tile's logits, then as Normal;
 //   Mode::Normal  P = exp2((S - m_ref) c), l += rowsum(P), O^T += V^T P^T;
 //   Mode::MaxOnly m_ref = max(m_ref, maximum of this tile's logits) only.
-template <Mode MODE, int D, int BLK>
-__device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* st, int kbase, int qc, int hh,
-                                             int lane, float scale_log2) {
+template <Mode MODE, int ST, int D, int BLK>
+__device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, float scale_log2) {
   using F = Fa<D, BLK>;
   f32x16 sacc[F::KTW][F::QT];
 #pragma unroll
@@ -189,13 +205,10 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
   // K fragments are read kKAhead d-steps ahead of their MFMAs; the scheduling
   // fences (which let vector ALU work move across) keep that order, so the
   // LDS latency is covered by the MFMAs in between.
-  uint4 kf[F::DS][F::KTW];
+  bf16x8 kf[F::DS][F::KTW];
   auto kread = [&](int s) {
 #pragma unroll
-    for (int kt = 0; kt < F::KTW; ++kt) {
-      const int row = kbase + 32 * kt + qc;
-      kf[s][kt] = st[row * F::NCH + ((2 * s + hh) ^ F::swz_k(row))];
-    }
+    for (int kt = 0; kt < F::KTW; ++kt) kf[s][kt] = lds_read_b128(w.ko[s] + ST * F::T + kt * 32 * F::NCH * 16);
   };
 #pragma unroll
   for (int s = 0; s < kKAhead && s < F::DS; ++s) kread(s);
@@ -207,7 +220,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
     for (int kt = 0; kt < F::KTW; ++kt)
 #pragma unroll
       for (int qt = 0; qt < F::QT; ++qt)
-        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s][kt]), w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
+        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][kt], w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0x406);
   }
 
@@ -232,12 +245,6 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
   // V^T operand for 16-key step ps and d tile dt: two transpose reads of keys
   // kbase + 16ps + 8half + 4hh + 0..3, columns d = 32dt + 16gd + i.  The
   // column swizzle depends only on the lane (key % 4 is fixed per lane).
-  const int grp = lane >> 4, j = lane & 15;
-  const int gd = grp & 1;
-  const int key0 = kbase + 4 * hh + (j >> 2);
-  const lds_u8_t* vbase = (const lds_u8_t*)(const lds_void_t*)st + F::TILE_CHUNKS * 16 + key0 * F::NCH * 16 +
-                          8 * (j & 1);
-  const int vsw = F::swz_v(key0);
   float lsum[F::QT];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) lsum[qt] = 0.f;
@@ -256,12 +263,11 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
     }
 #pragma unroll
     for (int dt = 0; dt < F::DT; ++dt) {
-      const int c = (4 * dt + 2 * gd + ((j & 3) >> 1)) ^ vsw;
       i16x4 part[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
         part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(vbase + (16 * ps + 8 * half) * F::NCH * 16 + c * 16));
+            (lds_i16x4_t*)(uintptr_t)(w.vo[dt] + ST * F::T + (16 * ps + 8 * half) * F::NCH * 16));
       bf16x8 a;
       __builtin_memcpy(&a, part, 16);
 #pragma unroll
@@ -281,36 +287,40 @@ __device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, const uint4* 
 // reads the other; one barrier per block.  FIRST_MODE applies to the first
 // listed block, MODE to the rest.
 template <Mode FIRST_MODE, Mode MODE, int D, int BLK>
-__device__ __forceinline__ void run_pass(WaveState<D, BLK>& w, uint4 (*stages)[2 * Fa<D, BLK>::TILE_CHUNKS],
-                                         const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
+__device__ __forceinline__ void run_pass(WaveState<D, BLK>& w, uint32_t lds0, const uint16_t* __restrict__ kh,
+                                         const uint16_t* __restrict__ vh,
                                          const __attribute__((address_space(4))) int32_t* list, int cnt, int nk,
-                                         int wave, const DmaOffsets<D, BLK>& dma, int kbase, int qc, int hh, int lane,
-                                         float scale_log2) {
+                                         int wave, const DmaOffsets<D, BLK>& dma, float scale_log2) {
   auto next_valid = [&](int t) {
     while (t < cnt && (unsigned)list[t] >= (unsigned)nk) ++t;
     return t;
   };
   int t = next_valid(0);
-  if (t < cnt) issue_tile<D, BLK>(stages[0], kh, vh, list[t], wave, dma);
+  if (t >= cnt) return;
+  issue_tile<0, D, BLK>(lds0, kh, vh, list[t], wave, dma);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int buf = 0;
-  if (FIRST_MODE != MODE && t < cnt) {  // peeled first block
-    const int tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<D, BLK>(stages[1], kh, vh, list[tn], wave, dma);
-    compute_tile<FIRST_MODE, D, BLK>(w, stages[0], kbase, qc, hh, lane, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    buf = 1;
-    t = tn;
-  }
+  // peeled first block (stage 0), then two blocks per turn (stages 1, 0) so
+  // that every LDS address is a loop-invariant register plus an immediate
+  int tn = next_valid(t + 1);
+  if (tn < cnt) issue_tile<1, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
+  compute_tile<FIRST_MODE, 0, D, BLK>(w, scale_log2);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  t = tn;
   while (t < cnt) {
-    const int tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<D, BLK>(stages[buf ^ 1], kh, vh, list[tn], wave, dma);
-    compute_tile<MODE, D, BLK>(w, stages[buf], kbase, qc, hh, lane, scale_log2);
+    tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<0, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
+    compute_tile<MODE, 1, D, BLK>(w, scale_log2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
+    t = tn;
+    if (t >= cnt) break;
+    tn = next_valid(t + 1);
+    if (tn < cnt) issue_tile<1, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
+    compute_tile<MODE, 0, D, BLK>(w, scale_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     t = tn;
   }
 }
@@ -343,7 +353,8 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
     float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   using F = Fa<D, BLK>;
-  __shared__ uint4 stages[2][2 * F::TILE_CHUNKS];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS_BYTES];
+  const uint32_t lds0 = lds_addr(lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -376,11 +387,26 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
       for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
   }
 
+#pragma unroll
+  for (int s = 0; s < F::DS; ++s) {
+    const int r = kbase + qc;
+    w.ko[s] = lds0 + (uint32_t)(r * F::NCH + ((2 * s + hh) ^ F::swz_k(r))) * 16u;
+  }
+  {
+    const int grp = lane >> 4, j = lane & 15;
+    const int gd = grp & 1;
+    const int key0 = kbase + 4 * hh + (j >> 2);
+    const int vsw = F::swz_v(key0);
+#pragma unroll
+    for (int dt = 0; dt < F::DT; ++dt) {
+      const int c = (4 * dt + 2 * gd + ((j & 3) >> 1)) ^ vsw;
+      w.vo[dt] = lds0 + F::V0 + (uint32_t)(key0 * F::NCH * 16 + 8 * (j & 1) + c * 16);
+    }
+  }
   DmaOffsets<D, BLK> dma;
   dma.init(wave, lane);
   w.bad = false;
-  run_pass<Mode::First, Mode::Normal, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
-                                              scale_log2);
+  run_pass<Mode::First, Mode::Normal, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
   if (__syncthreads_or(w.bad)) {
     // Rare: some logit exceeded the first block's maximum by more than 40
     // log2-units.  Find each query's true maximum, then redo the row at it.
@@ -393,15 +419,13 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
     }
-    run_pass<Mode::MaxOnly, Mode::MaxOnly, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
-                                                   scale_log2);
-    run_pass<Mode::Normal, Mode::Normal, D, BLK>(w, stages, kh, vh, list, cnt, nk, wave, dma, kbase, qc, hh, lane,
-                                                 scale_log2);
+    run_pass<Mode::MaxOnly, Mode::MaxOnly, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
+    run_pass<Mode::Normal, Mode::Normal, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
   }
 
   // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0 through LDS.
-  float* xo = reinterpret_cast<float*>(stages[0]);  // [qg][dt][qt][r][lane]
-  float* xm = reinterpret_cast<float*>(stages[1]);  // m: [qg][qt][lane], then l: [qg][qt][lane]
+  float* xo = reinterpret_cast<float*>(lds);           // [qg][dt][qt][r][lane]: blk*d floats = both K stages
+  float* xm = reinterpret_cast<float*>(lds + F::V0);  // m: [qg][qt][lane], then l: [qg][qt][lane]
   float lw[F::QT];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) lw[qt] = w.l[qt] + __shfl_xor(w.l[qt], 32);
