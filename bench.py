@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
-    ap.add_argument("--cold-reps", type=int, default=10, help="layers timed after a 1 GiB cache-flushing write")
+    ap.add_argument("--cold-reps", type=int, default=20, help="layers timed after a 1 GiB cache-flushing write")
     ap.add_argument("--no-probe", action="store_true", help="skip the MFMA-only peak probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counter scaling)")
@@ -134,7 +134,29 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cold_ms.append(e0.elapsed_time(e1))
-    del scratch
+    # measured device-copy bandwidth (1 GiB read + 1 GiB written per copy): the practical HBM ceiling
+    dst = torch.empty_like(scratch)
+    dst.copy_(scratch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(scratch)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * scratch.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # measured read-only streaming bandwidth (velox_hbm_read_probe over the 1 GiB buffer): the
+    # reference for the read-dominated routing phase
+    read_by_grid = {}
+    for grid in (512, 1024, 2048, 4096, 8192):
+        velox.hbm_read_probe(scratch, grid=grid, stream=stream)
+        e0.record(stream)
+        for _ in range(5):
+            velox.hbm_read_probe(scratch, grid=grid, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_by_grid[grid] = scratch.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    read_grid, read_gbs = max(read_by_grid.items(), key=lambda kv: kv[1])
+    del scratch, dst
 
     cnt = kv_cnt.cpu().numpy()
     f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
@@ -176,7 +198,10 @@ def main():
         "flops_dense": f_dense,
         "route_hbm": {"bytes": route_bytes, "achieved_GBs": round(route_bytes / (route_avg * 1e-3) / 1e9, 1),
                       "peak_GBs": PEAK_HBM_GBS,
-                      "frac": round(route_bytes / (route_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                      "frac": round(route_bytes / (route_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "measured_copy_GBs": round(copy_gbs, 1), "measured_read_GBs": round(read_gbs, 1),
+                      "measured_read_grid": read_grid,
+                      "frac_of_measured_read": round(route_bytes / (route_avg * 1e-3) / 1e9 / read_gbs, 4)},
         "roofline": {
             "kernel": "velox_sparse_fa (sparse_fa_bf16_kernel)" if bf else "sparse_fa_f32_kernel",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

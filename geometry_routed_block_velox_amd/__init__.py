@@ -26,7 +26,7 @@ from dataclasses import dataclass
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
     "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits", "score",
-    "frustum_overlap", "mfma_probe",
+    "frustum_overlap", "mfma_probe", "hbm_read_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +108,8 @@ def lib():
         L.velox_sparse_attn_split.restype = C.c_int
         L.velox_mfma_probe.argtypes = [C.c_int32, C.c_int32, V, V, V]
         L.velox_mfma_probe.restype = C.c_int
+        L.velox_hbm_read_probe.argtypes = [V, C.c_size_t, C.c_int32, V, V]
+        L.velox_hbm_read_probe.restype = C.c_int
         L.velox_status_string.argtypes = [C.c_int]
         L.velox_status_string.restype = C.c_char_p
         L.velox_last_hip_error.argtypes = []
@@ -359,6 +361,18 @@ def mfma_probe(grid: int, iters: int, stream=None):
     sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
     _raise(lib().velox_mfma_probe(int(grid), int(iters), _ptr(clocks), _ptr(sink), _stream(stream)), "velox_mfma_probe")
     return clocks
+
+
+def hbm_read_probe(buf, grid: int = 2048, stream=None):
+    """velox_hbm_read_probe: stream-read every byte of the device tensor `buf`; returns the
+    per-thread float32 sums (grid*256) of the 16-byte words each thread read."""
+    torch = _torch()
+    _dev(buf, "buf")
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _raise(lib().velox_hbm_read_probe(_ptr(buf), nbytes, int(grid), _ptr(sink), _stream(stream)),
+           "velox_hbm_read_probe")
+    return sink
 
 
 def auto_splits(p: Problem, num_cus: int | None = None) -> int:

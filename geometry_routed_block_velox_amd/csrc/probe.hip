@@ -1,6 +1,7 @@
+// Measurement aids beside the published peaks.
+//
 // velox_mfma_probe: an MFMA-only kernel that measures the bf16 matrix-core
-// rate and the shader clock the chip sustains under that load, as the
-// measured reference beside the published peak.
+// rate and the shader clock the chip sustains under that load.
 //
 // Every wave runs `iters` rounds of 16 independent v_mfma_f32_32x32x16_bf16
 // (four accumulator chains, operands in registers, no memory traffic), and
@@ -8,6 +9,12 @@
 // (s_memtime) and the elapsed 100 MHz reference clock (s_memrealtime).  The
 // caller times the launch with events; FLOPs = grid * 4 waves * iters * 16 *
 // 32768.
+//
+// velox_hbm_read_probe: a read-only streaming kernel (each workgroup reads a
+// contiguous slice with 16-byte loads, sixteen in flight per thread) that
+// measures the HBM read bandwidth a kernel can reach, the reference for
+// read-dominated kernels such as the block scoring (a device copy mixes reads
+// and writes).
 #include "velox_internal.h"
 
 namespace velox {
@@ -47,7 +54,37 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, int64_t* __r
   }
 }
 
+template <int U>
+__global__ __launch_bounds__(256) void hbm_read_probe_kernel(const float4* __restrict__ p, long long n4,
+                                                             float* __restrict__ sink) {
+  // Workgroup g reads the contiguous slice [g*per, (g+1)*per) of the buffer,
+  // U 16-byte loads per thread in flight, consecutive threads on consecutive words.
+  const long long per = (n4 + gridDim.x - 1) / gridDim.x;
+  const long long begin = (long long)blockIdx.x * per;
+  const long long end = begin + per < n4 ? begin + per : n4;
+  long long i = begin + threadIdx.x;
+  float acc = 0.f;
+  for (; i + (U - 1) * 256 < end; i += U * 256) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+  }
+  for (; i < end; i += 256) {
+    const float4 a = p[i];
+    acc += (a.x + a.y) + (a.z + a.w);
+  }
+  sink[(long long)blockIdx.x * 256 + threadIdx.x] = acc;  // keeps the loads alive
+}
+
 }  // namespace
+
+hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, int grid, float* sink, hipStream_t s) {
+  hipLaunchKernelGGL(hbm_read_probe_kernel<16>, dim3(grid), dim3(256), 0, s, static_cast<const float4*>(buf),
+                     (long long)(bytes / 16), sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(int grid, int iters, int64_t* clocks, float* sink, hipStream_t s) {
   hipLaunchKernelGGL(mfma_probe_kernel, dim3(grid), dim3(256), 0, s, iters, clocks, sink);

@@ -212,6 +212,14 @@ velox_status velox_mfma_probe(int32_t grid, int32_t iters, int64_t* clocks, floa
   return hip_status(velox::launch_mfma_probe(grid, iters, clocks, sink, reinterpret_cast<hipStream_t>(stream)));
 }
 
+velox_status velox_hbm_read_probe(const void* buf, size_t bytes, int32_t grid, float* sink,
+                                  velox_stream_t stream) {
+  if (!buf || !sink) return VELOX_ERR_NULL_POINTER;
+  if (grid < 1 || grid > 65536 || bytes == 0 || bytes % 16) return VELOX_ERR_BAD_SHAPE;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return VELOX_ERR_MISALIGNED;
+  return hip_status(velox::launch_hbm_read_probe(buf, bytes, grid, sink, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* velox_status_string(velox_status s) {
   switch (s) {
     case VELOX_OK: return "ok";

@@ -21,6 +21,7 @@ hipError_t launch_frustum_overlap(const velox_problem& p, const float* yaw, cons
                                   const float* query_depth, float fov, float* overlap, uint8_t* covered,
                                   hipStream_t s);
 hipError_t launch_mfma_probe(int grid, int iters, int64_t* clocks, float* sink, hipStream_t s);
+hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, int grid, float* sink, hipStream_t s);
 hipError_t launch_modulate_select(const velox_problem& p, const float* scores, const float* overlap,
                                   const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
 // splits == 0: one workgroup per row, direct output.  splits > 0: split-KV with

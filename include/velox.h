@@ -260,6 +260,17 @@ velox_status velox_sparse_attn_split(const velox_problem *p, const void *q, cons
  * iters >= 1 (else VELOX_ERR_BAD_SHAPE). */
 velox_status velox_mfma_probe(int32_t grid, int32_t iters, int64_t *clocks, float *sink, velox_stream_t stream);
 
+/* Measurement aid (not part of the layer): a read-only streaming kernel of
+ * `grid` workgroups x 256 threads that reads every 16-byte word of `buf`
+ * (device, `bytes` long, 16-byte aligned, bytes a non-zero multiple of 16)
+ * once with 16-byte loads and writes one float per thread to sink (device,
+ * grid*256 floats: that thread's sum of the words it read as float32), so the
+ * caller can time the read bandwidth a kernel reaches (bytes / event time)
+ * next to the published 8 TB/s.  1 <= grid <= 65536 (else
+ * VELOX_ERR_BAD_SHAPE); NULL pointers give VELOX_ERR_NULL_POINTER, a
+ * misaligned buf VELOX_ERR_MISALIGNED. */
+velox_status velox_hbm_read_probe(const void *buf, size_t bytes, int32_t grid, float *sink, velox_stream_t stream);
+
 /* Static English description of a status code. */
 const char *velox_status_string(velox_status s);
 
