@@ -60,7 +60,6 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 // d-steps by which the K fragment reads run ahead of their score MFMAs.

@@ -194,10 +194,16 @@ def test_unsorted_and_repeated_lists():
 
 
 @pytest.mark.parametrize("case", ["dominant-block", "two-close-blocks", "float32-overflow"])
-def test_logits_far_above_first_block_recompute_row(case):
+@pytest.mark.parametrize("base,extra", [("small", False), ("mid", False), ("mid", True)])
+def test_logits_far_above_first_block_recompute_row(case, base, extra):
     """Logits more than 40 log2-units above the first listed block's maximum make
-    the kernel redo the row at the true maximum; the result must still match."""
-    cfg = get_config("small").with_(heads=2, chunk_tokens=128, past_chunks=4)
+    the kernel redo the row at the true maximum; the result must still match.
+    d = 64 / blk = 64 and d = 128 / blk = 128 kernels, lists of 4 and 5 blocks
+    (both exits of the two-blocks-per-turn loop)."""
+    if base == "small":
+        cfg = get_config("small").with_(heads=2, chunk_tokens=128, past_chunks=4)
+    else:
+        cfg = get_config("mid").with_(heads=2, chunk_tokens=256, past_chunks=4)
     x = make_inputs(cfg)
     from synth import f32_to_bf16_bits
     q = np.ones((1, cfg.heads, cfg.chunk_tokens, cfg.head_dim), np.float32)
@@ -216,6 +222,9 @@ def test_logits_far_above_first_block_recompute_row(case):
         k[:, :, 2 * blk:3 * blk] = 4.0               # logit 32
         k[:, :, 5 * blk:6 * blk] = 3.875             # logit 31, both blocks matter
         lists = [0, 2, 5, 7]
+    if extra:
+        lists = lists + [cfg.nk - 1]
+    say(f"{base} d{cfg.head_dim} blk{cfg.block}: {case}, list {lists}")
     qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
     idx = np.broadcast_to(np.array(lists, np.int32), (1, cfg.heads, cfg.nq, len(lists))).copy()
     cnt = np.full((1, cfg.heads, cfg.nq), len(lists), np.int32)
