@@ -577,11 +577,13 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
   const int t = (int)(tok % BLK);
   const float* pl = part_lse + row * splits * BLK + t;
   float mx = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(size_t)s * BLK]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
   if (mx > -__builtin_inff()) {
     const float* po = part_o + (row * splits * BLK + t) * D + d;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) {
       const float ls = pl[(size_t)s * BLK];
       if (ls == -__builtin_inff()) continue;
