@@ -115,38 +115,83 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const typename E::T* __r
   wave_pool<E, D, BLK>(k + ((size_t)bh * nk + j) * BLK * D, kbar + ((size_t)bh * cache_blocks + j) * D, lane);
 }
 
-// s[i, j0+jj] = <qs_i, ks_jj> / sqrt(d) for the jn blocks staged in LDS (rows of D+1 floats).
+// Row pitch (floats) of the pooled rows staged in LDS: 16-byte aligned rows whose
+// starting banks differ by 4, so the 16-byte reads of up to 16 rows at once are
+// conflict-free.
+template <int D>
+constexpr int kLD = D + 4;
+
+// s[i, j0+jj] = <qs_i, ks_jj> / sqrt(d) for the jn blocks staged in LDS.  Each
+// thread computes a 2 x 2 patch (query rows i, i + ceil(nq/2); blocks jj,
+// jj + JB/2) from 16-byte LDS reads, so every operand read feeds two FMAs;
+// each dot product is one FMA chain over e = 0..D-1 in order.
 template <int D>
 __device__ __forceinline__ void score_rows(const float* qs, const float* ks, int nq, int jn, int j0, int nk,
                                            float* __restrict__ sh) {
-  constexpr int LD = D + 1;
+  constexpr int LD = kLD<D>;
+  static_assert(kJB % 2 == 0 && D % 4 == 0, "bad scoring patch");
   const float rs = 1.0f / sqrtf((float)D);
-  for (int pi = threadIdx.x; pi < nq * kJB; pi += 256) {
-    const int i = pi / kJB, jj = pi % kJB;
-    if (jj < jn) {
-      const float* a = qs + i * LD;
-      const float* b = ks + jj * LD;
-      float dot = 0.f;
-#pragma unroll 16
-      for (int e = 0; e < D; ++e) dot += a[e] * b[e];
-      sh[(size_t)i * nk + j0 + jj] = dot * rs;
+  constexpr int JP = kJB / 2;  // block pairs per workgroup
+  const int ip_n = (nq + 1) / 2;
+  for (int pt = threadIdx.x; pt < ip_n * JP; pt += 256) {
+    // patch (i0, i0 + ip_n) x (jj0, jj0 + JP): the 16 blocks read together are consecutive rows
+    const int i0 = pt / JP, jj0 = pt % JP;
+    if (jj0 >= jn) continue;
+    const int i1 = i0 + ip_n < nq ? i0 + ip_n : i0, jj1 = jj0 + JP < jn ? jj0 + JP : jj0;
+    const float4* a0 = reinterpret_cast<const float4*>(qs + i0 * LD);
+    const float4* a1 = reinterpret_cast<const float4*>(qs + i1 * LD);
+    const float4* b0 = reinterpret_cast<const float4*>(ks + jj0 * LD);
+    const float4* b1 = reinterpret_cast<const float4*>(ks + jj1 * LD);
+    float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < D / 4; ++e) {
+      const float4 x0 = a0[e], x1 = a1[e], y0 = b0[e], y1 = b1[e];
+      d00 = __builtin_fmaf(x0.x, y0.x, d00);
+      d01 = __builtin_fmaf(x0.x, y1.x, d01);
+      d10 = __builtin_fmaf(x1.x, y0.x, d10);
+      d11 = __builtin_fmaf(x1.x, y1.x, d11);
+      d00 = __builtin_fmaf(x0.y, y0.y, d00);
+      d01 = __builtin_fmaf(x0.y, y1.y, d01);
+      d10 = __builtin_fmaf(x1.y, y0.y, d10);
+      d11 = __builtin_fmaf(x1.y, y1.y, d11);
+      d00 = __builtin_fmaf(x0.z, y0.z, d00);
+      d01 = __builtin_fmaf(x0.z, y1.z, d01);
+      d10 = __builtin_fmaf(x1.z, y0.z, d10);
+      d11 = __builtin_fmaf(x1.z, y1.z, d11);
+      d00 = __builtin_fmaf(x0.w, y0.w, d00);
+      d01 = __builtin_fmaf(x0.w, y1.w, d01);
+      d10 = __builtin_fmaf(x1.w, y0.w, d10);
+      d11 = __builtin_fmaf(x1.w, y1.w, d11);
+    }
+    float* r0 = sh + (size_t)i0 * nk + j0;
+    r0[jj0] = d00 * rs;
+    if (jj1 != jj0) r0[jj1] = d01 * rs;
+    if (i1 != i0) {
+      float* r1 = sh + (size_t)i1 * nk + j0;
+      r1[jj0] = d10 * rs;
+      if (jj1 != jj0) r1[jj1] = d11 * rs;
     }
   }
 }
 
+// Copy n pooled rows (D floats each, contiguous in global memory) into LDS rows of pitch kLD<D>, 16 bytes
+// per load.
 template <int D>
-__device__ __forceinline__ void stage_qbar(const float* __restrict__ qh, float* qs, int nq) {
-  constexpr int LD = D + 1;
-  for (int x = threadIdx.x; x < nq * D; x += 256) qs[(x / D) * LD + x % D] = qh[x];
+__device__ __forceinline__ void stage_rows(const float* __restrict__ src, float* dst, int n) {
+  constexpr int LD = kLD<D>, C4 = D / 4;
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll 4
+  for (int x = threadIdx.x; x < n * C4; x += 256)
+    *reinterpret_cast<float4*>(dst + (x / C4) * LD + (x % C4) * 4) = s4[x];
 }
 
-// grid = (ceil(nk / JB), B*H); 256 threads; dynamic LDS (nq + JB) * (D + 1) floats.
+// grid = (ceil(nk / JB), B*H); 256 threads; dynamic LDS (nq + JB) * kLD<D> floats.
 template <class E, int D, int BLK>
 __global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* __restrict__ k,
                                                           const float* __restrict__ qbar,
                                                           float* __restrict__ scores, int nq, int nk) {
   extern __shared__ float lds[];
-  constexpr int LD = D + 1;  // padded row: consecutive rows fall in different banks
+  constexpr int LD = kLD<D>;
   float* qs = lds;
   float* ks = lds + nq * LD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -154,7 +199,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(const typename E::T* _
   const int j0 = blockIdx.x * kJB;
   const int jn = min(kJB, nk - j0);
 
-  stage_qbar<D>(qbar + (size_t)bh * nq * D, qs, nq);
+  stage_rows<D>(qbar + (size_t)bh * nq * D, qs, nq);
   const typename E::T* kh = k + (size_t)bh * nk * BLK * D;
   for (int jj = wave; jj < jn; jj += 4) wave_pool<E, D, BLK>(kh + (size_t)(j0 + jj) * BLK * D, ks + jj * LD, lane);
   __syncthreads();
@@ -169,15 +214,14 @@ __global__ __launch_bounds__(256) void cached_score_kernel(const float* __restri
                                                            float* __restrict__ scores, int nq, int nk,
                                                            int cache_blocks, int nscore) {
   extern __shared__ float lds[];
-  constexpr int LD = D + 1;
+  constexpr int LD = kLD<D>;
   float* qs = lds;
   float* ks = lds + nq * LD;
   const int bh = blockIdx.y;
   const int j0 = blockIdx.x * kJB;
   const int jn = min(kJB, nscore - j0);
-  stage_qbar<D>(qbar + (size_t)bh * nq * D, qs, nq);
-  const float* kc = kbar + ((size_t)bh * cache_blocks + j0) * D;
-  for (int x = threadIdx.x; x < jn * D; x += 256) ks[(x / D) * LD + x % D] = kc[x];
+  stage_rows<D>(qbar + (size_t)bh * nq * D, qs, nq);
+  stage_rows<D>(kbar + ((size_t)bh * cache_blocks + j0) * D, ks, jn);
   __syncthreads();
   score_rows<D>(qs, ks, nq, jn, j0, nk, scores + (size_t)bh * nq * nk);
 }
@@ -192,7 +236,7 @@ hipError_t pool_q(const Dims& x, const void* q, float* qbar, hipStream_t s) {
 
 template <class E, int D, int BLK>
 hipError_t score(const Dims& x, const void* k, const float* qbar, float* scores, hipStream_t s) {
-  const size_t lds = (size_t)(x.nq + kJB) * (D + 1) * sizeof(float);
+  const size_t lds = (size_t)(x.nq + kJB) * kLD<D> * sizeof(float);
   hipLaunchKernelGGL((block_score_kernel<E, D, BLK>), dim3((x.nk + kJB - 1) / kJB, x.B * x.H), dim3(256), lds, s,
                      static_cast<const typename E::T*>(k), qbar, scores, x.nq, x.nk);
   return hipGetLastError();
@@ -242,7 +286,7 @@ hipError_t launch_pool_keys(const velox_problem& p, const void* k, float* kbar, 
 hipError_t launch_cached_score(const velox_problem& p, const float* kbar, int cache_blocks, const float* qbar,
                                float* scores, int nscore, hipStream_t s) {
   const Dims x = dims(p);
-  const size_t lds = (size_t)(x.nq + kJB) * (x.d + 1) * sizeof(float);
+  const size_t lds = (size_t)(x.nq + kJB) * (x.d + 4) * sizeof(float);
   const dim3 grid((nscore + kJB - 1) / kJB, x.B * x.H);
   if (x.d == 128)
     hipLaunchKernelGGL(cached_score_kernel<128>, grid, dim3(256), lds, s, kbar, qbar, scores, x.nq, x.nk,
