@@ -1,0 +1,90 @@
+"""Host-side logic that needs no GPU: workload sizes, generator determinism and
+recipe, and the benchmark's own guards.
+
+* Derived sizes of the five workloads (block counts, executed and dense FLOPs)
+  against the values computed by hand from their shapes: the headline keeps
+  256 of 1568 KV blocks and executes 1.649 TFLOP of 10.10 TFLOP dense.
+* The generator is deterministic per seed and independent of its thread count;
+  uncovered query blocks follow the stated rounding (round(p * nq) per
+  rollout); frustum workloads mark a row covered exactly when some overlap is
+  positive.
+* bench.py refuses more than one GPU before touching the GPU, and reports
+  HBM traffic only while the profiled kernel source is unchanged.
+"""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from synth import get_config, make_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("name,nq,nk,f_exec,f_dense", [
+    ("tiny", 4, 36, 50_331_648, 150_994_944),
+    ("small", 16, 208, 3_221_225_472, 13_958_643_712),
+    ("mid", 16, 400, 137_438_953_472, 858_993_459_200),
+    ("headline", 32, 1568, 1_649_267_441_664, 10_101_763_080_192),
+    ("stress", 32, 3104, 3_298_534_883_328, 39_994_735_460_352),
+])
+def test_workload_sizes(name, nq, nk, f_exec, f_dense):
+    cfg = get_config(name)
+    assert (cfg.nq, cfg.nk) == (nq, nk)
+    assert cfg.flops_exec() == f_exec
+    assert cfg.flops_dense() == f_dense
+    # every executed tile is blk x blk: F_exec = 4 d blk^2 * rows * k_eff
+    assert f_exec == 4 * cfg.head_dim * cfg.block ** 2 * cfg.rows * cfg.k_eff
+
+
+def test_generator_is_deterministic_and_thread_independent():
+    cfg = get_config("small").with_(heads=3)
+    a = make_inputs(cfg, threads=1)
+    b = make_inputs(cfg, threads=3)
+    for name in ("q", "k", "v", "overlap", "covered"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    c = make_inputs(cfg, seeds=(cfg.seeds[0] + 1,), threads=1)
+    assert not np.array_equal(a.q, c.q)
+
+
+@pytest.mark.parametrize("name,uncovered", [("tiny", 1), ("small", 3)])
+def test_uncovered_count_rounding(name, uncovered):
+    cfg = get_config(name)
+    x = make_inputs(cfg)
+    assert int((x.covered == 0).sum()) == uncovered * cfg.batch
+    assert x.overlap.min() >= 0.0 and x.overlap.max() <= 1.0
+
+
+def test_frustum_coverage_rule():
+    cfg = get_config("mid").with_(heads=1)
+    x = make_inputs(cfg)
+    assert np.array_equal(x.covered.astype(bool), (x.overlap > 0).any(axis=2))
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _bench_module():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_bench_traffic_only_for_the_profiled_source(tmp_path):
+    bench = _bench_module()
+    other = tmp_path / "other.hip"
+    other.write_text("// not the profiled kernel\n")
+    assert bench.traffic_from_profiles(str(other)) is None
+    import json
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_sparse_fa_headline.json")))
+    src = os.path.join(ROOT, "geometry_routed_block_velox_amd", "csrc", "sparse_fa.hip")
+    expected = rec["hbm_bytes_per_launch"] if rec["kernel_source_sha"] == bench.file_sha(src) else None
+    assert bench.traffic_from_profiles(src) == expected
