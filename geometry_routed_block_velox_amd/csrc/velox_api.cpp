@@ -37,6 +37,7 @@ velox_status check_problem(const velox_problem* p, bool routing) {
   const int64_t nk = ((int64_t)p->past_chunks + 1) * nq;
   if (p->top_k < (routing ? nq : 1)) return VELOX_ERR_BAD_SHAPE;
   if (nq > VELOX_MAX_QUERY_BLOCKS || nk > VELOX_MAX_KV_BLOCKS) return VELOX_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->heads > VELOX_MAX_HEADS_TOTAL) return VELOX_ERR_UNSUPPORTED;
   // Grid sizes: one workgroup per row must fit the 32-bit grid.
   if ((int64_t)p->batch * p->heads * nq > INT32_MAX / 2) return VELOX_ERR_UNSUPPORTED;
   return VELOX_OK;

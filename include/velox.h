@@ -73,9 +73,11 @@ typedef enum velox_dtype { VELOX_F32 = 0, VELOX_BF16 = 1 } velox_dtype;
 typedef enum velox_modulation { VELOX_MOD_SCALE = 0, VELOX_MOD_LOG_PROB = 1 } velox_modulation;
 
 /* Built configurations: d in {64, 128}, blk in {64, 128}, both dtypes.
- * Limits: nq <= VELOX_MAX_QUERY_BLOCKS, nk <= VELOX_MAX_KV_BLOCKS. */
+ * Limits: nq <= VELOX_MAX_QUERY_BLOCKS, nk <= VELOX_MAX_KV_BLOCKS, B*H <= VELOX_MAX_HEADS_TOTAL
+ * (the scoring kernels put the (b,h) pair on the second grid axis). */
 #define VELOX_MAX_QUERY_BLOCKS 64
 #define VELOX_MAX_KV_BLOCKS 8192
+#define VELOX_MAX_HEADS_TOTAL 65535
 
 typedef struct velox_problem {
   int32_t batch;        /* B: independent rollouts                                         */

@@ -48,6 +48,7 @@ def test_check_accepts_every_workload():
     ("alpha", float("inf"), Status.BAD_SHAPE), ("head_dim", 96, Status.UNSUPPORTED),
     ("block", 32, Status.UNSUPPORTED), ("dtype", 7, Status.UNSUPPORTED),
     ("chunk_tokens", 128 * 65, Status.UNSUPPORTED), ("past_chunks", 300, Status.UNSUPPORTED),
+    ("heads", 65536, Status.UNSUPPORTED),
 ])
 def test_check_rejects(field, value, status):
     p = headline()
