@@ -165,6 +165,23 @@ def _dev(t, name, dtype=None, ndim=None):
     return t
 
 
+def _out(t, name, shape, dtype):
+    """A caller-provided output (or workspace) buffer: GPU, contiguous, exact dtype and shape."""
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _workspace(ws, need, device):
+    """The caller's workspace if it is a large enough GPU uint8 buffer, else a new one."""
+    torch = _torch()
+    if ws is None or ws.numel() < need:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace", torch.uint8, ndim=1)
+    return ws
+
+
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
@@ -209,11 +226,10 @@ def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_s
         kv_idx = torch.empty((B, H, p.nq, top_k), dtype=torch.int32, device=q.device)
         kv_cnt = torch.empty((B, H, p.nq), dtype=torch.int32, device=q.device)
     else:
-        kv_idx, kv_cnt = out
+        kv_idx = _out(out[0], "kv_idx", (B, H, p.nq, top_k), torch.int32)
+        kv_cnt = _out(out[1], "kv_cnt", (B, H, p.nq), torch.int32)
     scores = torch.empty((B, H, p.nq, p.nk), dtype=torch.float32, device=q.device) if return_scores else None
-    need = velox_route_workspace_bytes(p)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, velox_route_workspace_bytes(p), q.device)
     st = lib().velox_route(C.byref(p), _ptr(q), _ptr(k), _ptr(overlap), _ptr(covered), _ptr(kv_idx), _ptr(kv_cnt),
                            _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "velox_route")
@@ -233,9 +249,7 @@ def score(q, k, block: int, scores=None, workspace=None, stream=None):
     _dev(scores, "scores", torch.float32, ndim=4)
     if tuple(scores.shape) != (B, H, p.nq, p.nk):
         raise ValueError(f"scores must be [{B},{H},{p.nq},{p.nk}]")
-    need = velox_route_workspace_bytes(p)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, velox_route_workspace_bytes(p), q.device)
     _raise(lib().velox_score(C.byref(p), _ptr(q), _ptr(k), _ptr(scores), _ptr(workspace), workspace.numel(),
                              _stream(stream)), "velox_score")
     return scores
@@ -262,7 +276,8 @@ def frustum_overlap(yaw, past_depth, query_depth, fov_deg: float, out=None, stre
         overlap = torch.empty((B, nq, C_), dtype=torch.float32, device=yaw.device)
         covered = torch.empty((B, nq), dtype=torch.uint8, device=yaw.device)
     else:
-        overlap, covered = out
+        overlap = _out(out[0], "overlap", (B, nq, C_), torch.float32)
+        covered = _out(out[1], "covered", (B, nq), torch.uint8)
     st = lib().velox_frustum_overlap(C.byref(p), _ptr(yaw), _ptr(past_depth if C_ > 0 else None),
                                      _ptr(query_depth), float(fov_deg), _ptr(overlap if C_ > 0 else None),
                                      _ptr(covered), _stream(stream))
@@ -314,11 +329,10 @@ def route_cached(q, kbar, past_chunks: int, overlap, covered, block: int, top_k:
         kv_idx = torch.empty((B, H, p.nq, top_k), dtype=torch.int32, device=q.device)
         kv_cnt = torch.empty((B, H, p.nq), dtype=torch.int32, device=q.device)
     else:
-        kv_idx, kv_cnt = out
+        kv_idx = _out(out[0], "kv_idx", (B, H, p.nq, top_k), torch.int32)
+        kv_cnt = _out(out[1], "kv_cnt", (B, H, p.nq), torch.int32)
     scores = torch.empty((B, H, p.nq, p.nk), dtype=torch.float32, device=q.device) if return_scores else None
-    need = velox_route_workspace_bytes(p)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, velox_route_workspace_bytes(p), q.device)
     st = lib().velox_route_cached(C.byref(p), _ptr(q), _ptr(kbar), kbar.shape[2], _ptr(overlap), _ptr(covered),
                                   _ptr(kv_idx), _ptr(kv_cnt), _ptr(scores), _ptr(workspace), workspace.numel(),
                                   _stream(stream))
@@ -400,7 +414,7 @@ def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, o
         raise ValueError("k/v shape mismatch")
     if tuple(kv_idx.shape[:3]) != (B, H, p.nq) or tuple(kv_cnt.shape) != (B, H, p.nq):
         raise ValueError("kv_idx/kv_cnt shape mismatch")
-    o = out if out is not None else torch.empty_like(q)
+    o = _out(out, "out", q.shape, q.dtype) if out is not None else torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     if splits is None:
         st = lib().velox_sparse_attn(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(o),
@@ -408,9 +422,7 @@ def sparse_attn(q, k, v, kv_idx, kv_cnt, block: int, return_lse: bool = False, o
         _raise(st, "velox_sparse_attn")
     else:
         n = auto_splits(p) if splits == "auto" else int(splits)
-        need = velox_sparse_attn_split_workspace_bytes(p, n)
-        if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, velox_sparse_attn_split_workspace_bytes(p, n), q.device)
         st = lib().velox_sparse_attn_split(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), n,
                                            _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
         _raise(st, "velox_sparse_attn_split")
