@@ -34,7 +34,11 @@
  * examples for modulation and selection (tests/golden/), brute-force
  * subset enumeration for the selection, keep-all against brute-force
  * dense attention, closed-form two-key and zero-query attention, and the
- * skipped-block poison invariant.
+ * skipped-block poison invariant; for the sign-safe modulation a worked
+ * example and a brute-force softmax check; for the frustum overlap closed
+ * forms and a Monte Carlo estimate.  Every function here has such a pin.
+ * Against Velox as published, parity unpinned: the article prints no
+ * formula, worked example or intermediate value for these steps.
  *
  * dtype codes: 0 = float32, 1 = bfloat16 bit patterns (uint16).
  * All functions return 0 on success and a negative value on bad arguments.
