@@ -34,9 +34,13 @@
  * examples for modulation and selection (tests/golden/), brute-force
  * subset enumeration for the selection, keep-all against brute-force
  * dense attention, closed-form two-key and zero-query attention, and the
- * skipped-block poison invariant; for the sign-safe modulation a worked
- * example and a brute-force softmax check; for the frustum overlap closed
- * forms and a Monte Carlo estimate.  Every function here has such a pin.
+ * skipped-block poison invariant; closed forms over several batch
+ * elements, heads and query blocks (every (b,h), query block and KV block
+ * carrying its own constant) for pooling, scores, listed and dense
+ * attention, so that every row and head stride is pinned; for the
+ * sign-safe modulation a worked example and a brute-force softmax check;
+ * for the frustum overlap closed forms and a Monte Carlo estimate.  Every
+ * function here has such a pin.
  * Against Velox as published, parity unpinned: the article prints no
  * formula, worked example or intermediate value for these steps.
  *
@@ -325,14 +329,20 @@ int velox_oracle_select(const double *m, int64_t rows, int nk, int k, int32_t *k
  *   out: [ntok, d]; lse (optional): [ntok]
  * For a token t of query block i = t / blk, with U the union of the kept
  * blocks' tokens: l_u = <q_t, k_u>/sqrt(d), M = max l_u, w_u = exp(l_u - M),
- * out = sum w_u v_u / sum w_u, lse = M + log(sum w_u).  No causal mask. */
+ * out = sum w_u v_u / sum w_u, lse = M + log(sum w_u).  No causal mask.
+ * Lists follow the library's contract for caller-made lists: the first
+ * min(max(kv_cnt, 0), kmax) entries are read and an entry outside
+ * [0, N/blk) names no block and is skipped; a row left with no block gets
+ * out = 0 and lse = -inf. */
 int velox_oracle_attn(const void *q, const void *k, const void *v, int dtype, int B, int H, int T, int64_t N,
                       int d, int blk, const int32_t *kv_idx, const int32_t *kv_cnt, int kmax, int64_t ntok,
                       const int64_t *tok, double *out, double *lse) {
   if (!q || !k || !v || !kv_idx || !kv_cnt || !out || B < 0 || H < 0 || d < 1 || blk < 1 || T % blk)
     return -1;
   if (!tok && ntok != (int64_t)B * H * T) return -1;
+  if (kmax < 1 || N % blk) return -1;
   const int nq = T / blk;
+  const int64_t nkb = N / blk;
   const double scale = 1.0 / sqrt((double)d);
   int fail = 0;
 #pragma omp parallel for schedule(dynamic, 8) reduction(| : fail)
@@ -341,19 +351,16 @@ int velox_oracle_attn(const void *q, const void *k, const void *v, int dtype, in
     const int64_t bh = f / T;
     const int t = (int)(f % T);
     const int64_t row = bh * nq + t / blk;
-    const int cnt = kv_cnt[row];
+    const int cnt = kv_cnt[row] < 0 ? 0 : (kv_cnt[row] > kmax ? kmax : kv_cnt[row]);
     const int32_t *list = kv_idx + row * kmax;
-    if (cnt < 1 || cnt > kmax) {
-      fail = 1;
-      continue;
-    }
-    double *logit = (double *)malloc(sizeof(double) * (size_t)cnt * blk);
+    double *logit = (double *)malloc(sizeof(double) * (size_t)(cnt > 0 ? cnt : 1) * blk);
     if (!logit) {
       fail = 1;
       continue;
     }
     double M = -INFINITY;
     for (int c = 0; c < cnt; ++c) {
+      if (list[c] < 0 || list[c] >= nkb) continue;
       for (int u = 0; u < blk; ++u) {
         const int64_t key = (int64_t)list[c] * blk + u;
         double dot = 0.0;
@@ -365,6 +372,7 @@ int velox_oracle_attn(const void *q, const void *k, const void *v, int dtype, in
     double wsum = 0.0;
     for (int e = 0; e < d; ++e) out[n * d + e] = 0.0;
     for (int c = 0; c < cnt; ++c) {
+      if (list[c] < 0 || list[c] >= nkb) continue;
       for (int u = 0; u < blk; ++u) {
         const int64_t key = (int64_t)list[c] * blk + u;
         const double w = exp(logit[c * blk + u] - M);
@@ -372,8 +380,9 @@ int velox_oracle_attn(const void *q, const void *k, const void *v, int dtype, in
         for (int e = 0; e < d; ++e) out[n * d + e] += w * elem(v, dtype, (bh * N + key) * d + e);
       }
     }
-    for (int e = 0; e < d; ++e) out[n * d + e] /= wsum;
-    if (lse) lse[n] = M + log(wsum);
+    if (wsum > 0.0)
+      for (int e = 0; e < d; ++e) out[n * d + e] /= wsum;
+    if (lse) lse[n] = wsum > 0.0 ? M + log(wsum) : -INFINITY;
     free(logit);
   }
   return fail ? -2 : 0;

@@ -70,6 +70,145 @@ def test_score_constant_blocks_closed_form():
     assert np.array_equal(s[0, 0, 0], [0.5, -0.25])
 
 
+# ---------------------------------------------------------------- several batch elements, heads and rows
+
+# B = 2, H = 3, nq = 4 query blocks, nk = 12 KV blocks, blk = 4, d = 16 (so 1/sqrt(d) = 1/4 exactly).
+# Every (b, h) pair bh = b*H + h, every query block i and every KV block j carries its own constant, and
+# each block adds a zero-mean ramp (-1.5, -0.5, 0.5, 1.5) in another coordinate, so the pooled means, the
+# scores and the attention outputs below are closed forms in bh, i and j: a slip in any row, head or
+# block stride of the oracle changes them.
+_MB, _MH, _MNQ, _MC, _MBLK, _MD = 2, 3, 4, 2, 4, 16
+_MT = _MNQ * _MBLK
+_MN = (_MC + 1) * _MT
+_MNK = _MN // _MBLK
+_RAMP = np.arange(_MBLK) - (_MBLK - 1) / 2
+
+
+def _multi_head_qk():
+    q = np.zeros((_MB, _MH, _MT, _MD), np.float32)
+    k = np.zeros((_MB, _MH, _MN, _MD), np.float32)
+    for b in range(_MB):
+        for h in range(_MH):
+            bh = b * _MH + h
+            for i in range(_MNQ):
+                q[b, h, i * _MBLK:(i + 1) * _MBLK, 0] = (bh + 1) * (i + 1)
+                q[b, h, i * _MBLK:(i + 1) * _MBLK, 1] = _RAMP
+            for j in range(_MNK):
+                k[b, h, j * _MBLK:(j + 1) * _MBLK, 0] = j + 1 + 7 * bh
+                k[b, h, j * _MBLK:(j + 1) * _MBLK, 2] = _RAMP
+    return q, k
+
+
+def test_pool_and_scores_multi_head_closed_form():
+    q, k = _multi_head_qk()
+    qbar, kbar = O.pool(q, _MBLK), O.pool(k, _MBLK)
+    s = O.scores(qbar, kbar)
+    assert s.shape == (_MB, _MH, _MNQ, _MNK)
+    for b, h, i, j in itertools.product(range(_MB), range(_MH), range(_MNQ), range(_MNK)):
+        bh = b * _MH + h
+        e_q = np.zeros(_MD); e_q[0] = (bh + 1) * (i + 1)
+        e_k = np.zeros(_MD); e_k[0] = j + 1 + 7 * bh
+        assert np.array_equal(qbar[b, h, i], e_q) and np.array_equal(kbar[b, h, j], e_k)
+        assert s[b, h, i, j] == (bh + 1) * (i + 1) * (j + 1 + 7 * bh) / 4.0, (b, h, i, j)
+
+
+def _multi_head_lists():
+    # a different list per row (b, h, i): distinct blocks, not sorted, lengths 1..4
+    idx = np.full((_MB, _MH, _MNQ, 4), -1, np.int32)
+    cnt = np.zeros((_MB, _MH, _MNQ), np.int32)
+    for b, h, i in itertools.product(range(_MB), range(_MH), range(_MNQ)):
+        bh = b * _MH + h
+        n = 1 + (bh + i) % 4
+        blocks = [(5 * bh + 3 * i + 7 * c) % _MNK for c in range(n)]
+        assert len(set(blocks)) == n
+        idx[b, h, i, :n] = blocks
+        cnt[b, h, i] = n
+    return idx, cnt
+
+
+def test_attention_multi_head_zero_query_is_mean_of_kept_blocks():
+    # Q = 0: every kept key has weight 1, so out = mean over the kept blocks of V's block constant
+    # 10*bh + j (the within-block ramp averages to 0) and lse = log(cnt * blk).
+    q = np.zeros((_MB, _MH, _MT, _MD), np.float32)
+    k = np.random.default_rng(40).standard_normal((_MB, _MH, _MN, _MD)).astype(np.float32)
+    v = np.zeros((_MB, _MH, _MN, _MD), np.float32)
+    for b, h, j in itertools.product(range(_MB), range(_MH), range(_MNK)):
+        v[b, h, j * _MBLK:(j + 1) * _MBLK, 0] = 10 * (b * _MH + h) + j
+        v[b, h, j * _MBLK:(j + 1) * _MBLK, 1] = _RAMP
+    idx, cnt = _multi_head_lists()
+    out, lse = O.attn(q, k, v, idx, cnt, _MBLK)
+    for b, h, i in itertools.product(range(_MB), range(_MH), range(_MNQ)):
+        kept = idx[b, h, i, :cnt[b, h, i]]
+        expect = np.zeros(_MD); expect[0] = np.mean(10 * (b * _MH + h) + kept)
+        rows = out[b, h, i * _MBLK:(i + 1) * _MBLK]
+        assert np.allclose(rows, expect[None], rtol=0, atol=1e-12), (b, h, i)
+        assert np.allclose(lse[b, h, i * _MBLK:(i + 1) * _MBLK], math.log(cnt[b, h, i] * _MBLK), rtol=0, atol=1e-13)
+    # the dense brute force over every key of a head: the mean of all its blocks' constants
+    dout, dlse = O.dense_attn(q, k, v)
+    for b, h in itertools.product(range(_MB), range(_MH)):
+        assert np.allclose(dout[b, h, :, 0], 10 * (b * _MH + h) + (_MNK - 1) / 2, rtol=0, atol=1e-12)
+        assert np.allclose(dlse[b, h], math.log(_MN), rtol=0, atol=1e-13)
+
+
+def test_attention_multi_head_block_constant_keys_closed_form():
+    # Keys constant over each block (kappa(bh, j) e0) and queries a(bh, t) e0: every key of block j has
+    # the logit a*kappa/4, so attention over tokens reduces to a softmax over the kept blocks, each
+    # counted blk times: out_0 = sum_j w_j c_j / sum_j w_j with w_j = exp(a kappa_j / 4) and c_j the
+    # block constant of V, and lse = log(blk * sum_j exp(a kappa_j / 4)).
+    q = np.zeros((_MB, _MH, _MT, _MD), np.float32)
+    k = np.zeros((_MB, _MH, _MN, _MD), np.float32)
+    v = np.zeros((_MB, _MH, _MN, _MD), np.float32)
+    kappa = lambda bh, j: ((j + 2 * bh) % 5 - 2) * 1.5
+    a = lambda bh, t: ((t + 3 * bh) % 7 - 3) * 0.75
+    for b, h in itertools.product(range(_MB), range(_MH)):
+        bh = b * _MH + h
+        for t in range(_MT):
+            q[b, h, t, 0] = a(bh, t)
+        for j in range(_MNK):
+            k[b, h, j * _MBLK:(j + 1) * _MBLK, 0] = kappa(bh, j)
+            v[b, h, j * _MBLK:(j + 1) * _MBLK, 0] = 10 * bh + j
+            v[b, h, j * _MBLK:(j + 1) * _MBLK, 3] = _RAMP
+    idx, cnt = _multi_head_lists()
+    out, lse = O.attn(q, k, v, idx, cnt, _MBLK)
+    for b, h, t in itertools.product(range(_MB), range(_MH), range(_MT)):
+        bh, i = b * _MH + h, t // _MBLK
+        kept = idx[b, h, i, :cnt[b, h, i]]
+        w = np.array([math.exp(a(bh, t) * kappa(bh, j) / 4.0) for j in kept])
+        c = np.array([10 * bh + j for j in kept], np.float64)
+        expect = np.zeros(_MD); expect[0] = (w * c).sum() / w.sum()
+        assert np.allclose(out[b, h, t], expect, rtol=0, atol=1e-12), (b, h, t)
+        assert abs(lse[b, h, t] - math.log(_MBLK * w.sum())) <= 1e-12
+    # the dense brute force is the same closed form over every block of the head
+    dout, dlse = O.dense_attn(q, k, v)
+    for b, h, t in itertools.product(range(_MB), range(_MH), range(_MT)):
+        bh = b * _MH + h
+        w = np.array([math.exp(a(bh, t) * kappa(bh, j) / 4.0) for j in range(_MNK)])
+        c = 10.0 * bh + np.arange(_MNK)
+        assert abs(dout[b, h, t, 0] - (w * c).sum() / w.sum()) <= 1e-12, (b, h, t)
+        assert abs(dlse[b, h, t] - math.log(_MBLK * w.sum())) <= 1e-12
+
+
+def test_attention_list_contract_invalid_entries_and_empty_rows():
+    # entries outside [0, nk) name no block and are skipped; a count above the stride is clamped; a row
+    # with no valid block gives out = 0 and lse = -inf (the library's contract for caller-made lists)
+    q, k = _multi_head_qk()
+    v = np.random.default_rng(41).standard_normal((_MB, _MH, _MN, _MD)).astype(np.float32)
+    idx, cnt = _multi_head_lists()
+    ref, ref_lse = O.attn(q, k, v, idx, cnt, _MBLK)
+    bad = np.full((_MB, _MH, _MNQ, 8), -1, np.int32)
+    bad[..., 1:5] = idx
+    bad[..., 0] = _MNK          # first entry out of range on the high side
+    bad[..., 5] = -7            # and on the low side
+    out, lse = O.attn(q, k, v, bad, cnt + 2, _MBLK)
+    assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+    empty = np.full((_MB, _MH, _MNQ, 2), -1, np.int32)
+    out, lse = O.attn(q, k, v, empty, np.full((_MB, _MH, _MNQ), 2, np.int32), _MBLK)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+    out, lse = O.attn(q, k, v, idx, np.full((_MB, _MH, _MNQ), 99, np.int32), _MBLK)
+    full, full_lse = O.attn(q, k, v, idx, np.full((_MB, _MH, _MNQ), 4, np.int32), _MBLK)
+    assert np.array_equal(out, full) and np.array_equal(lse, full_lse)
+
+
 # ---------------------------------------------------------------- modulation + selection, worked examples
 
 def _one_row(s, overlap, covered, alpha, k, C):
