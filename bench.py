@@ -33,7 +33,6 @@ def parse():
     ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
     ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
     ap.add_argument("--cold-reps", type=int, default=20, help="layers timed after a 1 GiB cache-flushing write")
-    ap.add_argument("--no-probe", action="store_true", help="skip the MFMA-only peak probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counter scaling)")
     return ap.parse_args()
@@ -144,18 +143,6 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 2.0 * scratch.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # measured read-only streaming bandwidth (velox_hbm_read_probe over the 1 GiB buffer): the
-    # reference for the read-dominated routing phase
-    read_by_grid = {}
-    for grid in (512, 1024, 2048, 4096, 8192):
-        velox.hbm_read_probe(scratch, grid=grid, stream=stream)
-        e0.record(stream)
-        for _ in range(5):
-            velox.hbm_read_probe(scratch, grid=grid, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        read_by_grid[grid] = scratch.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    read_grid, read_gbs = max(read_by_grid.items(), key=lambda kv: kv[1])
     del scratch, dst
 
     cnt = kv_cnt.cpu().numpy()
@@ -199,9 +186,8 @@ def main():
         "route_hbm": {"bytes": route_bytes, "achieved_GBs": round(route_bytes / (route_avg * 1e-3) / 1e9, 1),
                       "peak_GBs": PEAK_HBM_GBS,
                       "frac": round(route_bytes / (route_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                      "measured_copy_GBs": round(copy_gbs, 1), "measured_read_GBs": round(read_gbs, 1),
-                      "measured_read_grid": read_grid,
-                      "frac_of_measured_read": round(route_bytes / (route_avg * 1e-3) / 1e9 / read_gbs, 4)},
+                      "measured_copy_GBs": round(copy_gbs, 1),
+                      "frac_of_measured_copy": round(route_bytes / (route_avg * 1e-3) / 1e9 / copy_gbs, 4)},
         "roofline": {
             "kernel": "velox_sparse_fa (sparse_fa_bf16_kernel)" if bf else "sparse_fa_f32_kernel",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -211,11 +197,6 @@ def main():
             "kv_union_blocks": union_blocks,
         },
     }
-
-    if not args.no_probe:
-        probe = bench_mfma_probe(velox, stream)
-        res["mfma_probe"] = probe
-        res["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / probe["tflops"], 4)
 
     if not args.no_context:
         # keep-all through the same kernel: the same-kernel "dense" comparison at this chunk
@@ -246,27 +227,6 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
     print(json.dumps(res), flush=True)
-
-
-def bench_mfma_probe(velox, stream, grid=256, iters=20000):
-    """The MFMA-only kernel on every CU: the bf16 rate and shader clock this chip sustains."""
-    import numpy as np
-    import torch
-    velox.mfma_probe(grid, 100, stream=stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    clocks = velox.mfma_probe(grid, iters, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    c = clocks.cpu().numpy().astype(np.float64)
-    ghz = float(np.median(c[:, 0] / (c[:, 1] / 100e6)) / 1e9)
-    flops = grid * 4.0 * iters * 16 * 32768
-    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "sclk_ghz": round(ghz, 3), "grid": grid, "iters": iters,
-            "frac_of_published_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "note": "v_mfma_f32_32x32x16_bf16 only, operands in registers; shader clock from s_memtime vs "
-                    "s_memrealtime inside the kernel"}
 
 
 def bench_overlap_builder(velox, cfg, x, q, k, ws, stream, reps=20):

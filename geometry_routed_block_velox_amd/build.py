@@ -9,8 +9,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvelox.so")
-SOURCES = ["velox_api.cpp", "block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip", "probe.hip"]
+# Host-only C++ (g++: argument checks and the launching entry points) and HIP
+# kernels (hipcc for gfx950).
+HOST_SOURCES = ["velox_check.cpp", "velox_api.cpp"]
+HIP_SOURCES = ["block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip"]
+SOURCES = HOST_SOURCES + HIP_SOURCES
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -19,18 +25,26 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# the HIP runtime-API types of velox_launch.h, for the host compiler
+HOST_FLAGS = [
+    "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", os.path.join(ROCM, "include"),
+]
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in HOST_SOURCES:
+        cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "unknown target feature" not in l and "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+        raise RuntimeError(f"{cmd[0]} failed on {src}:\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
     return obj

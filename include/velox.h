@@ -90,7 +90,8 @@ typedef struct velox_problem {
   int32_t top_k;        /* kept KV blocks per row including the ncur current blocks
                            (top_k >= ncur); values above nk keep every block               */
   float alpha;          /* modulation strength, finite and >= 0                            */
-  velox_dtype dtype;    /* element type of Q, K, V and Out                                 */
+  int32_t dtype;        /* a velox_dtype: element type of Q, K, V and Out (an int32, so
+                           that any value a caller passes can be checked)                  */
   int32_t modulation;   /* a velox_modulation (0 = VELOX_MOD_SCALE when zero-initialised);
                            used by routing, must be valid everywhere                       */
 } velox_problem;
@@ -251,30 +252,8 @@ velox_status velox_sparse_attn_split(const velox_problem *p, const void *q, cons
                                      const int32_t *kv_idx, const int32_t *kv_cnt, int32_t num_splits, void *out,
                                      float *lse, void *workspace, size_t workspace_bytes, velox_stream_t stream);
 
-/* Measurement aid (not part of the layer): an MFMA-only kernel of `grid`
- * workgroups x 4 waves, each wave running iters x 16 independent
- * v_mfma_f32_32x32x16_bf16 with register operands, so the caller can measure
- * the bf16 matrix-core rate the chip sustains (FLOPs = grid*4*iters*16*32768,
- * timed with events on `stream`) next to the published peak.  Writes, per
- * workgroup, the elapsed shader clocks and elapsed 100 MHz reference clocks
- * of its first wave to clocks[2*wg], clocks[2*wg+1] (device, int64), and one
- * float per thread to sink (device, grid*256 floats).  1 <= grid <= 65536,
- * iters >= 1 (else VELOX_ERR_BAD_SHAPE). */
-velox_status velox_mfma_probe(int32_t grid, int32_t iters, int64_t *clocks, float *sink, velox_stream_t stream);
-
-/* Measurement aid (not part of the layer): a read-only streaming kernel of
- * `grid` workgroups x 256 threads that reads every 16-byte word of `buf`
- * (device, `bytes` long, 16-byte aligned, bytes a non-zero multiple of 16)
- * once with 16-byte loads and writes one float per thread to sink (device,
- * grid*256 floats: that thread's sum of the words it read as float32), so the
- * caller can time the read bandwidth a kernel reaches (bytes / event time)
- * next to the published 8 TB/s.  1 <= grid <= 65536 (else
- * VELOX_ERR_BAD_SHAPE); NULL pointers give VELOX_ERR_NULL_POINTER, a
- * misaligned buf VELOX_ERR_MISALIGNED. */
-velox_status velox_hbm_read_probe(const void *buf, size_t bytes, int32_t grid, float *sink, velox_stream_t stream);
-
 /* Static English description of a status code. */
-const char *velox_status_string(velox_status s);
+const char *velox_status_string(int32_t status);
 
 /* hipError_t of the last failed launch on the calling thread (0 = none). */
 int velox_last_hip_error(void);

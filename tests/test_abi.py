@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"velox_check", "velox_route", "velox_select", "velox_sparse_attn", "velox_route_workspace_bytes",
             "velox_status_string", "velox_last_hip_error", "velox_pool_keys", "velox_route_cached", "velox_sparse_attn_split",
             "velox_sparse_attn_split_workspace_bytes", "velox_sparse_attn_auto_splits", "velox_score",
-            "velox_frustum_overlap", "velox_mfma_probe", "velox_hbm_read_probe"} <= set(names)
+            "velox_frustum_overlap"} <= set(names)
     lib = C.CDLL(velox.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -185,28 +185,8 @@ def test_score_and_overlap_builder_validate_before_launch():
     assert L.velox_last_hip_error() == 0
 
 
-def test_mfma_probe_validates_before_launch():
-    L = velox.lib()
-    fake = C.c_void_p(0x100000)
-    assert L.velox_mfma_probe(0, 10, fake, fake, None) == Status.BAD_SHAPE
-    assert L.velox_mfma_probe(256, 0, fake, fake, None) == Status.BAD_SHAPE
-    assert L.velox_mfma_probe(256, 10, None, fake, None) == Status.NULL_POINTER
-
-
 def test_status_strings():
     L = velox.lib()
     for s in range(7):
         assert L.velox_status_string(s)
     assert L.velox_status_string(99) == b"unknown status"
-
-
-def test_hbm_read_probe_validates_before_launch():
-    L = velox.lib()
-    fake = C.c_void_p(4096)
-    assert L.velox_hbm_read_probe(None, 1024, 16, fake, None) == Status.NULL_POINTER
-    assert L.velox_hbm_read_probe(fake, 1024, 16, None, None) == Status.NULL_POINTER
-    assert L.velox_hbm_read_probe(fake, 0, 16, fake, None) == Status.BAD_SHAPE
-    assert L.velox_hbm_read_probe(fake, 1000, 16, fake, None) == Status.BAD_SHAPE
-    assert L.velox_hbm_read_probe(fake, 1024, 0, fake, None) == Status.BAD_SHAPE
-    assert L.velox_hbm_read_probe(fake, 1024, 70000, fake, None) == Status.BAD_SHAPE
-    assert L.velox_hbm_read_probe(C.c_void_p(4100), 1024, 16, fake, None) == Status.MISALIGNED
