@@ -8,33 +8,36 @@
 // computed with an online softmax over the list, one KV block (= one tile)
 // at a time.  No causal mask.
 //
-// bf16 kernel (sparse_fa_bf16_kernel): one workgroup per row, 2*blk/32 waves
-// (8 at blk = 128, i.e. two waves per SIMD).
-//  * Work split: wave w owns 32 queries (query group w % (blk/32)) and one key
-//    half (w / (blk/32)) of every tile: 32 queries x 64 keys at blk = 128.
-//    Two waves per SIMD let one wave's softmax and LDS waits overlap the
-//    other's MFMAs; the price is twice the LDS operand reads per MFMA of a
-//    64-query split (measured: the two-wave split is faster).  The two key
-//    halves keep independent online softmax states that are merged once at
-//    the end of the row.
-//  * Scores are formed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: lane l of an accumulator holds query l%32 and
+// bf16 kernel (sparse_fa_bf16_kernel): one workgroup per row, one wave per
+// SIMD (4 waves at blk = 128), each wave holding up to 512 registers.
+//  * Work split: wave w owns 64 queries (query group w % (blk/64), two
+//    32-query MFMA tiles) and one key half (w / (blk/64)) of every tile:
+//    64 queries x 64 keys at blk = 128.  Every K or V operand read from LDS
+//    feeds both query tiles, so a tile costs 128 KiB of LDS operand reads
+//    (K and V halves read once per query group).  The two key halves keep
+//    independent online softmax states that are merged once at the end of
+//    the row.
+//  * Software pipeline inside each wave: iteration t computes the scores of
+//    listed block t+1 on the matrix cores, S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16, while the vector ALU turns the scores of block
+//    t into probabilities; then O^T += V^T P^T for block t.  The softmax of a
+//    block thus overlaps the score MFMAs of the next one without a second
+//    wave on the SIMD.  Lane l of a score accumulator holds query l%32 and
 //    keys 8(r/4) + 4(l/32) + r%4, so softmax statistics need one lane
 //    exchange (l <-> l^32) and output rescaling is a per-lane scalar.
-//  * O^T += V^T P^T takes P from the score registers as the B operand.  The
-//    contraction may visit keys in any order as long as both operands agree;
-//    the V^T operand is read from the row-major V tile with the LDS
-//    transpose read ds_read_b64_tr_b16, whose 16-lane groups return lane i
-//    four consecutive rows of column i -- exactly the accumulator's key order.
+//  * O^T += V^T P^T takes P from registers as the B operand.  The contraction
+//    may visit keys in any order as long as both operands agree; the V^T
+//    operand is read from the row-major V tile with the LDS transpose read
+//    ds_read_b64_tr_b16, whose 16-lane groups return lane i four consecutive
+//    rows of column i -- exactly the accumulator's key order.
 //  * K and V tiles go from HBM straight to LDS (global_load_lds_dwordx4, no
-//    register staging), double-buffered so that the loads of the next listed
-//    block overlap the MFMA work on the current one; one barrier per block.
-//    16-byte chunks are XOR-swizzled per row so that the MFMA operand reads
-//    of K and the transpose reads of V spread over the banks.  K operand
-//    fragments are read two MFMA steps ahead of their use.  Every LDS operand
-//    address is a per-lane register computed once per workgroup plus an
-//    instruction immediate (stage, key tile, 16-key step): the block loop is
-//    unrolled over the two stages, so it does no address arithmetic.
+//    register staging) into two K and two V slots, separate LDS arrays so
+//    that the compiler's wait counting knows a copy into one slot does not
+//    feed reads of another.  Iteration t copies K of block t+2 and V of block
+//    t+1 while it reads K of block t+1 and V of block t: one barrier per
+//    block, and a copy has a whole iteration to land.  16-byte chunks are
+//    XOR-swizzled per row so that the MFMA operand reads of K and the
+//    transpose reads of V spread over the banks.
 //  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
 //    Each wave fixes its softmax reference maximum m_ref per query from the
 //    first listed block (the exact maximum over that block, so the largest
@@ -42,10 +45,12 @@
 //    the loop: later probabilities exp2((s - m_ref) c) may exceed 1, which
 //    float32 sums and bf16 P (same exponent range as float32) hold with the
 //    same relative precision, and the final normalisation uses the same
-//    m_ref, so the result is the same softmax.  If any block's probability
-//    sum exceeds 2^40 (logits more than 40 log2-units above the first
-//    block's maximum), the workgroup reruns the row: a max-only sweep finds
-//    the true maximum, then a second pass uses it (all probabilities <= 1).
+//    m_ref, so the result is the same softmax.  The probability sums add the
+//    bf16-rounded P that the PV product uses (v_dot2_f32_bf16 against ones),
+//    so numerator and denominator carry the same weights.  If any block's
+//    probability sum exceeds 2^40 (logits more than 40 log2-units above the
+//    first block's maximum), the workgroup reruns the row: a max-only sweep
+//    finds the true maximum, then a second pass uses it (all P <= 1).
 //  * Workgroups are remapped so that the rows of one head run on one XCD and
 //    share its L2 while they walk their ascending block lists.
 // float32 kernel (sparse_fa_f32_kernel): one thread per query token, plain
@@ -56,45 +61,42 @@ namespace velox {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
-// d-steps by which the K fragment reads run ahead of their score MFMAs.
+// d-steps by which the K and Q fragment reads run ahead of their score MFMAs.
 constexpr int kKAhead = 2;
+// PV steps by which the V^T fragment reads run ahead of their MFMAs.
+constexpr int kVAhead = 6;
 
 // Per-block probability sum above which a row is recomputed at its true maximum.
 constexpr float kOverflowGuard = 1099511627776.0f;  // 2^40
 
 template <int D, int BLK>
 struct Fa {
-  static constexpr int QW = 32;                 // queries per wave
+  static constexpr int QT = 2;                  // 32-query MFMA tiles per wave
+  static constexpr int QW = 32 * QT;            // queries per wave
   static constexpr int NQG = BLK / QW;          // query groups
-  static constexpr int NW = 2 * NQG;            // waves per workgroup: query groups x two key halves
-  static constexpr int NT = NW * 64;
-  static constexpr int KW = BLK / 2;            // keys per wave and tile
-  static constexpr int QT = QW / 32;            // 32-query MFMA tiles per wave
+  static constexpr int KW = BLK / 2;            // keys per wave and tile (two key halves)
   static constexpr int KTW = KW / 32;           // 32-key MFMA tiles per wave
+  static constexpr int NW = 2 * NQG;            // waves per workgroup
+  static constexpr int NT = NW * 64;            // = 2 * BLK
   static constexpr int DS = D / 16;             // MFMA k-steps over d (scores)
   static constexpr int DT = D / 32;             // 32-row d tiles of O^T
   static constexpr int PS = KW / 16;            // MFMA k-steps over keys (PV)
   static constexpr int NCH = D / 8;             // 16-byte chunks per row
   static constexpr int TILE_CHUNKS = BLK * NCH; // per K (or V) tile
-  static constexpr int SEGS_PER_WAVE = TILE_CHUNKS / 64 / NW;  // 1 KiB DMA segments
-  static_assert(QT >= 1 && KTW >= 1 && NCH >= 8 && SEGS_PER_WAVE >= 1, "unsupported tile shape");
-  static constexpr int T = BLK * D * 2;             // bytes of one K (or V) tile
-  static constexpr int V0 = 2 * T, LDS_BYTES = 4 * T;  // K stages at 0 and T, V stages at 2T and 3T
+  static constexpr int SEGS = TILE_CHUNKS / 64 / NW;  // 1 KiB copies per wave and tile (K or V)
+  static constexpr int T = BLK * D * 2;         // bytes of one K (or V) tile
+  static_assert(NQG >= 1 && KTW >= 1 && NCH >= 8 && SEGS >= 1, "unsupported tile shape");
   static __device__ __forceinline__ int swz_k(int row) { return row & (NCH - 1); }
   static __device__ __forceinline__ int swz_v(int row) { return (4 * row) & (NCH - 1); }
 };
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -104,225 +106,484 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-// Issue the HBM -> LDS copies of KV block j (K into st[0, TILE), V into
-// st[TILE, 2*TILE)).  Lane l of DMA segment g writes 16-byte slot 64g + l,
-// i.e. row (64g + l) / NCH and physical chunk (64g + l) % NCH; it fetches the
-// logical chunk stored there under the row's swizzle.  Per-lane byte offsets
-// within the block are precomputed once per thread in DmaOffsets.
+// HBM -> LDS copies of KV blocks (buffer_load_dwordx4 ... lds: 16 bytes per
+// lane, copy g of a tile landing at LDS tile + 1 KiB * g + 16 * lane).  Lane
+// l of copy g writes LDS slot 64g + l, i.e. row slot / NCH and physical
+// chunk slot % NCH, and fetches the logical chunk stored there under the
+// row's swizzle: byte g * 1 KiB + sw(l, g) of the block, where sw depends on
+// g only through g mod P (the swizzle repeats every NCH rows for K and every
+// NCH/4 rows for V), so a lane keeps P offsets per tensor.  The buffer
+// resource spans one head of K (or V); a block is addressed by its scalar
+// byte offset, and offsets past the end read zeros.
 template <int D, int BLK>
-struct DmaOffsets {
+struct Copier {
   using F = Fa<D, BLK>;
-  uint32_t k[F::SEGS_PER_WAVE];
-  uint32_t v[F::SEGS_PER_WAVE];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  static constexpr int PK = F::NCH * F::NCH / 64 > 1 ? F::NCH * F::NCH / 64 : 1;
+  static constexpr int PV = F::NCH * F::NCH / 256 > 1 ? F::NCH * F::NCH / 256 : 1;
+  static_assert(F::SEGS % PK == 0 && F::SEGS % PV == 0, "copy period must divide the copies per wave");
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  uint32_t ko[PK], vo[PV];
+  int wave;
+
+  static __device__ __forceinline__ uint32_t sw(int lane, int g, bool is_v) {
+    const int slot = g * 64 + lane;
+    const int row = slot / F::NCH, pc = slot % F::NCH;
+    const int c = pc ^ (is_v ? F::swz_v(row) : F::swz_k(row));
+    return (uint32_t)(((row - g * 64 / F::NCH) * D + c * 8) * 2);
+  }
+  __device__ __forceinline__ void init(const uint16_t* kh, const uint16_t* vh, uint32_t head_bytes, int w, int lane) {
+    wave = w;
+    krs = __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, (int)head_bytes, 0x00020000);
+    vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, (int)head_bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < F::SEGS_PER_WAVE; ++i) {
-      const int slot = (wave * F::SEGS_PER_WAVE + i) * 64 + lane;
-      const int row = slot / F::NCH, pc = slot % F::NCH;
-      k[i] = (uint32_t)(row * D + (pc ^ F::swz_k(row)) * 8) * 2u;
-      v[i] = (uint32_t)(row * D + (pc ^ F::swz_v(row)) * 8) * 2u;
-    }
+    for (int i = 0; i < PK; ++i) ko[i] = (uint32_t)i * 1024u + sw(lane, i, false);
+#pragma unroll
+    for (int i = 0; i < PV; ++i) vo[i] = (uint32_t)i * 1024u + sw(lane, i, true);
   }
 };
 
-// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l
-// fetches gbase + voff and the data lands at LDS byte lds + 16*l.  Written as
-// inline asm so that the compiler's wait-count pass does not treat every
-// later LDS read as a possible consumer of the copy; the kernel waits for
-// the copies itself (s_waitcnt vmcnt(0)) before the barrier that publishes
-// the tile.  The instruction writes no VGPR.
-__device__ __forceinline__ void lds_dma16(uint32_t lds, const void* gbase, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds), "v"(voff), "s"(gbase)
-      : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-
-template <int ST, int D, int BLK>
-__device__ __forceinline__ void issue_tile(uint32_t lds0, const uint16_t* __restrict__ kh,
-                                           const uint16_t* __restrict__ vh, int j, int wave,
-                                           const DmaOffsets<D, BLK>& off) {
+// Copy i (0 <= i < SEGS) of this wave's share of block j's tile of tensor
+// WHAT (0 = K, 1 = V) into dst:
+// global byte j*T + g*1024 + sw(lane, g) = soff + (i % P)*1024 + sw(lane, i % P)
+// with g = wave*SEGS + i.
+template <int WHAT, int D, int BLK>
+__device__ __forceinline__ void copy_one(const Copier<D, BLK>& cp, unsigned char* dst, int j, int i) {
+  // The builtin exists only in the device compilation; the host pass of this
+  // HIP source never runs the kernel.
+#if defined(__HIP_DEVICE_COMPILE__)
   using F = Fa<D, BLK>;
-  const uint16_t* kb = kh + (size_t)j * BLK * D;
-  const uint16_t* vb = vh + (size_t)j * BLK * D;
-#pragma unroll
-  for (int i = 0; i < F::SEGS_PER_WAVE; ++i) {
-    const uint32_t seg = (uint32_t)(wave * F::SEGS_PER_WAVE + i) * 1024u;
-    lds_dma16(lds0 + ST * F::T + seg, kb, off.k[i]);
-    lds_dma16(lds0 + F::V0 + ST * F::T + seg, vb, off.v[i]);
-  }
+  const int g = cp.wave * F::SEGS + i;
+  constexpr int P = WHAT == 1 ? Copier<D, BLK>::PV : Copier<D, BLK>::PK;
+  const uint32_t soff = (uint32_t)j * (uint32_t)F::T + (uint32_t)(g - i % P) * 1024u;
+  if constexpr (WHAT == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.vrs, (lds_void_t*)(dst + g * 1024), 16, cp.vo[i % P], soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.krs, (lds_void_t*)(dst + g * 1024), 16, cp.ko[i % P], soff, 0, 0);
+#endif
 }
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+template <int WHAT, int D, int BLK>
+__device__ __forceinline__ void copy_tile(const Copier<D, BLK>& cp, unsigned char* dst, int j) {
+#pragma unroll
+  for (int i = 0; i < Fa<D, BLK>::SEGS; ++i) copy_one<WHAT, D, BLK>(cp, dst, j, i);
+}
 
-__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
-  const u32x4 x = *(const lds_u32x4_t*)(uintptr_t)addr;
+// The four LDS slots of a workgroup: K and V of two blocks in flight.
+struct Slots {
+  unsigned char* k[2];
+  unsigned char* v[2];
+};
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const unsigned char* p) {
+  const u32x4 x = *(const lds_u32x4_t*)p;
   bf16x8 r;
   __builtin_memcpy(&r, &x, 16);
   return r;
+}
+
+// Matrix-core products, written as inline assembly so that the register
+// files are fixed: score accumulators in VGPRs (the softmax reads them), the
+// Q fragments and the O accumulators in AGPRs.  The hazards the compiler
+// would otherwise handle are handled here:
+//  * a VALU write of a VGPR needs 2 wait states before an MFMA reads it: the
+//    PV product (B operand = probabilities just converted by the VALU) starts
+//    with s_nop 1;
+//  * an MFMA result needs up to 18 wait states before a VALU or an AGPR read
+//    uses it: fence_vgpr / fence_agpr wait that long and take the results as
+//    asm operands, so that the compiler cannot schedule a read above the wait
+//    (a plain asm with a memory clobber does not order register reads); in
+//    the pipelined loop the scores of a block are read one iteration later,
+//    after the PV MFMAs and a barrier, behind a fence that only orders;
+//  * back-to-back accumulation into the same registers is interlocked by the
+//    hardware, and every chain here interleaves at least three independent
+//    accumulators anyway;
+//  * the A and B operands are read when the MFMA issues, so their registers
+//    may be refilled right after it; a result that does not accumulate is
+//    early-clobber so that it never overlaps an operand.
+__device__ __forceinline__ void mfma_score_first(f32x16& acc, const bf16x8& kfrag, const bf16x8& qfrag) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(kfrag), "a"(qfrag));
+}
+__device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& kfrag, const bf16x8& qfrag) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kfrag), "a"(qfrag));
+}
+__device__ __forceinline__ void mfma_pv(f32x16& acc, const bf16x8& vfrag, const bf16x8& pfrag) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(vfrag), "v"(pfrag));
+}
+// Wait (WAIT = true: 18 wait states) for the MFMAs that last wrote `acc`,
+// as an asm that takes the accumulators as operands, so that no later read
+// of them can be scheduled above it.  With WAIT = false it only orders the
+// reads after this point (for results known to be complete).
+template <bool WAIT, int N0, int N1>
+__device__ __forceinline__ void fence_vgpr(f32x16 (&acc)[N0][N1]) {
+  if (WAIT)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc[0][0])::"memory");
+  else
+    asm volatile("" : "+v"(acc[0][0])::"memory");
+#pragma unroll
+  for (int a = 0; a < N0; ++a)
+#pragma unroll
+    for (int b = 0; b < N1; ++b)
+      if (a || b) asm volatile("" : "+v"(acc[a][b]));
+}
+template <int N0, int N1>
+__device__ __forceinline__ void fence_agpr(f32x16 (&acc)[N0][N1]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(acc[0][0])::"memory");
+#pragma unroll
+  for (int a = 0; a < N0; ++a)
+#pragma unroll
+    for (int b = 0; b < N1; ++b)
+      if (a || b) asm volatile("" : "+a"(acc[a][b]));
 }
 
 // Per-wave state of the online softmax over this wave's key half.
 template <int D, int BLK>
 struct WaveState {
   using F = Fa<D, BLK>;
-  bf16x8 qf[F::QT][F::DS];     // Q fragments: B operand of S^T = K Q^T
-  f32x16 oacc[F::DT][F::QT];   // O^T accumulators
+  bf16x8 qf[F::QT][F::DS];     // Q fragments (AGPRs): B operand of S^T = K Q^T
+  f32x16 oacc[F::DT][F::QT];   // O^T accumulators (AGPRs)
   float m[F::QT];              // reference maximum (raw logits) of query qc of tile qt
   float l[F::QT];              // this lane's partial sum of probabilities
   bool bad;                    // a probability sum crossed kOverflowGuard
-  // Per-lane LDS byte addresses in stage 0; stage, key tile, step and half are immediate offsets.
+  // Per-lane LDS byte offsets within a tile; key tile, step and half are immediate offsets.
   uint32_t ko[F::DS];          // K fragment of d-step s, key tile 0
   uint32_t vo[F::DT];          // first V^T transpose read of d tile dt
 };
 
-enum class Mode { First, Normal, MaxOnly };
-
-// One tile from the LDS stage st: S^T = K Q^T, then
-//   Mode::First   m_ref = maximum of this tile's logits, then as Normal;
-//   Mode::Normal  P = exp2((S - m_ref) c), l += rowsum(P), O^T += V^T P^T;
-//   Mode::MaxOnly m_ref = max(m_ref, maximum of this tile's logits) only.
-template <Mode MODE, int ST, int D, int BLK>
-__device__ __forceinline__ void compute_tile(WaveState<D, BLK>& w, float scale_log2) {
+template <int D, int BLK>
+__device__ __forceinline__ bf16x8 k_fragment(const WaveState<D, BLK>& w, const unsigned char* kt_base, int s, int kt) {
   using F = Fa<D, BLK>;
-  f32x16 sacc[F::KTW][F::QT];
-#pragma unroll
-  for (int kt = 0; kt < F::KTW; ++kt)
-#pragma unroll
-    for (int qt = 0; qt < F::QT; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][qt][r] = 0.f;
+  return lds_read_b128(kt_base + w.ko[s] + kt * 32 * F::NCH * 16);
+}
 
-  // K fragments are read kKAhead d-steps ahead of their MFMAs; the scheduling
-  // fences (which let vector ALU work move across) keep that order, so the
-  // LDS latency is covered by the MFMAs in between.
-  bf16x8 kf[F::DS][F::KTW];
-  auto kread = [&](int s) {
+// V^T operand for 16-key step ps and d tile dt: two transpose reads of keys
+// kbase + 16ps + 8half + 4hh + 0..3, columns d = 32dt + 16gd + i.
+template <int D, int BLK>
+__device__ __forceinline__ bf16x8 v_fragment(const WaveState<D, BLK>& w, const unsigned char* vt_base, int ps, int dt) {
+  using F = Fa<D, BLK>;
+  i16x4 part[2];
 #pragma unroll
-    for (int kt = 0; kt < F::KTW; ++kt) kf[s][kt] = lds_read_b128(w.ko[s] + ST * F::T + kt * 32 * F::NCH * 16);
-  };
-#pragma unroll
-  for (int s = 0; s < kKAhead && s < F::DS; ++s) kread(s);
+  for (int half = 0; half < 2; ++half)
+    part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(vt_base + w.vo[dt] + (16 * ps + 8 * half) * F::NCH * 16));
+  bf16x8 a;
+  __builtin_memcpy(&a, part, 16);
+  return a;
+}
+
+// S^T = K Q^T for the KV tile in LDS at kt_base (this wave's key half), into
+// sacc, with nothing else interleaved (prologue and rare paths).
+template <int D, int BLK>
+__device__ __forceinline__ void scores(const WaveState<D, BLK>& w, const unsigned char* kt_base,
+                                       f32x16 (&sacc)[Fa<D, BLK>::KTW][Fa<D, BLK>::QT]) {
+  using F = Fa<D, BLK>;
 #pragma unroll
   for (int s = 0; s < F::DS; ++s) {
-    if (s + kKAhead < F::DS) kread(s + kKAhead);
-    __builtin_amdgcn_sched_barrier(0x406);
+    bf16x8 kf[F::KTW];
+#pragma unroll
+    for (int kt = 0; kt < F::KTW; ++kt) kf[kt] = k_fragment<D, BLK>(w, kt_base, s, kt);
 #pragma unroll
     for (int kt = 0; kt < F::KTW; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < F::QT; ++qt)
-        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][kt], w.qf[qt][s], sacc[kt][qt], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0x406);
+      for (int qt = 0; qt < F::QT; ++qt) {
+        if (s == 0)
+          mfma_score_first(sacc[kt][qt], kf[kt], w.qf[qt][s]);
+        else
+          mfma_score(sacc[kt][qt], kf[kt], w.qf[qt][s]);
+      }
   }
+  fence_vgpr<true>(sacc);
+}
 
-  if constexpr (MODE != Mode::Normal) {
+// Per-query maximum of a score tile, over both lane halves.
+template <int D, int BLK>
+__device__ __forceinline__ void tile_max(const f32x16 (&sacc)[Fa<D, BLK>::KTW][Fa<D, BLK>::QT], float (&mx)[Fa<D, BLK>::QT]) {
+  using F = Fa<D, BLK>;
 #pragma unroll
-    for (int qt = 0; qt < F::QT; ++qt) {
-      float mx = sacc[0][qt][0];
+  for (int qt = 0; qt < F::QT; ++qt) {
+    float v = sacc[0][qt][0];
 #pragma unroll
-      for (int kt = 0; kt < F::KTW; ++kt)
+    for (int kt = 0; kt < F::KTW; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      w.m[qt] = MODE == Mode::First ? mx : fmaxf(w.m[qt], mx);
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[kt][qt][r]);
+    mx[qt] = fmaxf(v, __shfl_xor(v, 32));
+  }
+}
+
+// Softmax element e of a score tile: query tile qt, 16-key step ps, register
+// i of that step, e = (qt * PS + ps) * 8 + i.  pb[ps][qt] holds keys 16ps.. of
+// the tile, i.e. accumulator registers 8(ps%2).. of key tile ps/2.
+template <int D, int BLK>
+struct Softmax {
+  using F = Fa<D, BLK>;
+  static constexpr int NE = F::QT * F::PS * 8;
+  const f32x16 (&sacc)[F::KTW][F::QT];
+  bf16x8 (&pb)[F::PS][F::QT];
+  float mb[F::QT];
+  float scale_log2;
+  float p_even;  // probability of the last even element, packed with the next one
+  __device__ __forceinline__ void element(int e) {
+    const int i = e & 7, ps = (e >> 3) % F::PS, qt = (e >> 3) / F::PS;
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][qt][8 * (ps & 1) + i], scale_log2, -mb[qt]));
+    if ((i & 1) == 0) {
+      p_even = p;
+    } else {
+      pb[ps][qt][i - 1] = (__bf16)p_even;
+      pb[ps][qt][i] = (__bf16)p;
     }
   }
-  if constexpr (MODE == Mode::MaxOnly) return;
+};
 
-  float mb[F::QT];
+// Row sums of the bf16 probabilities of 16-key step ps (the weights the PV product uses).
+template <int D, int BLK>
+__device__ __forceinline__ void row_sums(const bf16x8 (&pb)[Fa<D, BLK>::PS][Fa<D, BLK>::QT], int ps,
+                                         float (&lsum)[Fa<D, BLK>::QT]) {
+  using F = Fa<D, BLK>;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int qt = 0; qt < F::QT; ++qt) mb[qt] = w.m[qt] * scale_log2;
+  for (int qt = 0; qt < F::QT; ++qt)
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const bf16x2 two = {pb[ps][qt][i], pb[ps][qt][i + 1]};
+      lsum[qt] = __builtin_amdgcn_fdot2_f32_bf16(two, ones, lsum[qt], false);
+    }
+}
 
-  // V^T operand for 16-key step ps and d tile dt: two transpose reads of keys
-  // kbase + 16ps + 8half + 4hh + 0..3, columns d = 32dt + 16gd + i.  The
-  // column swizzle depends only on the lane (key % 4 is fixed per lane).
-  float lsum[F::QT];
+// The row's list, consumed in order, valid entries only (ids in [0, nk);
+// anything else is skipped).  Entries come through a 64-entry window in one
+// VGPR (lane i: entry base + i) with a wave-uniform mask of its valid lanes;
+// an id is taken with v_readlane.  The next window is loaded one window
+// ahead with a vector load, so no scalar memory load is outstanding in the
+// block loop (it would force every LDS wait to drain completely).
+struct ListStream {
+  const int32_t* list;
+  int cnt, nk;
+  int base;       // list position of the window's first entry
+  int win, ahead; // this window's entries and the next window's (per lane)
+  uint64_t mask;  // valid lanes of this window not handed out yet
+
+  __device__ __forceinline__ int load(int b, int lane) const {
+    return b + lane < cnt ? list[b + lane] : -1;
+  }
+  __device__ __forceinline__ void start(int lane) {
+    base = 0;
+    win = load(0, lane);
+    ahead = load(64, lane);
+    mask = __builtin_amdgcn_ballot_w64((unsigned)win < (unsigned)nk);
+  }
+  // Number of valid entries in the whole list.
+  __device__ __forceinline__ int valid(int lane) const {
+    int c = 0;
+    for (int t = lane; t < cnt; t += 64) c += (unsigned)list[t] < (unsigned)nk;
 #pragma unroll
-  for (int qt = 0; qt < F::QT; ++qt) lsum[qt] = 0.f;
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    return __builtin_amdgcn_readfirstlane(c);
+  }
+  // The next valid id, or -1 past the end.
+  __device__ __forceinline__ int take(int lane) {
+    while (mask == 0) {
+      if (base + 64 >= cnt) return -1;
+      base += 64;
+      win = ahead;
+      ahead = load(base + 64, lane);
+      mask = __builtin_amdgcn_ballot_w64((unsigned)win < (unsigned)nk);
+    }
+    const int i = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    return __builtin_amdgcn_readlane(win, i);
+  }
+};
+
+// One software-pipelined pass over the row's listed blocks.  With FIRST the
+// reference maximum comes from the first listed block; otherwise w.m is
+// given.  Iteration t (block t of the valid entries, slots by parity):
+//   copies  K(t+2) -> K slot t%2, V(t+1) -> V slot (t+1)%2
+//   scores  S(t+1) from K slot (t+1)%2        (matrix cores)
+//   softmax P(t) from S(t)                   (vector ALU, overlapping)
+//   PV      O += V(t)^T P(t) from V slot t%2
+//   wait for the copies, barrier.
+template <int D, int BLK>
+struct Pass {
+  using F = Fa<D, BLK>;
+  WaveState<D, BLK>& w;
+  const Slots& sl;
+  ListStream& ls;
+  const Copier<D, BLK>& cp;
+  float scale_log2;
+
+  int fallback;  // a valid block id, copied for the phantom step past the end of the list
+
+  // O += V^T P^T for the V tile in LDS at vb and the row sums of P after
+  // each 16-key step.  V^T fragments are read kVAhead steps ahead through a
+  // ring; the caller may have issued the first kVAhead reads (vf) already.
+  static constexpr int NV = F::PS * F::DT;  // PV steps per block
+  __device__ __forceinline__ void pv_prefetch(bf16x8 (&vf)[kVAhead + 1], const unsigned char* vb) {
 #pragma unroll
-  for (int ps = 0; ps < F::PS; ++ps) {
-    // P for these 16 keys: accumulator registers 8(ps%2)..+7 of key tile ps/2.
-    bf16x8 pb[F::QT];
+    for (int n = 0; n < kVAhead && n < NV; ++n) vf[n] = v_fragment<D, BLK>(w, vb, n / F::DT, n % F::DT);
+  }
+  __device__ __forceinline__ void pv(const bf16x8 (&pb)[F::PS][F::QT], const unsigned char* vb,
+                                     bf16x8 (&vf)[kVAhead + 1]) {
+    float lsum[F::QT];
 #pragma unroll
-    for (int qt = 0; qt < F::QT; ++qt) {
+    for (int qt = 0; qt < F::QT; ++qt) lsum[qt] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][qt][8 * (ps & 1) + i], scale_log2, -mb[qt]));
-        lsum[qt] += p;
-        pb[qt][i] = (__bf16)p;
+    for (int ps = 0; ps < F::PS; ++ps) {
+#pragma unroll
+      for (int dt = 0; dt < F::DT; ++dt) {
+        const int n = ps * F::DT + dt, na = n + kVAhead;
+        if (na < NV) vf[na % (kVAhead + 1)] = v_fragment<D, BLK>(w, vb, na / F::DT, na % F::DT);
+#pragma unroll
+        for (int qt = 0; qt < F::QT; ++qt) mfma_pv(w.oacc[dt][qt], vf[n % (kVAhead + 1)], pb[ps][qt]);
+        if (dt == 0) row_sums<D, BLK>(pb, ps, lsum);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < F::DT; ++dt) {
-      i16x4 part[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(uintptr_t)(w.vo[dt] + ST * F::T + (16 * ps + 8 * half) * F::NCH * 16));
-      bf16x8 a;
-      __builtin_memcpy(&a, part, 16);
-#pragma unroll
-      for (int qt = 0; qt < F::QT; ++qt)
-        w.oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt], w.oacc[dt][qt], 0, 0, 0);
+    for (int qt = 0; qt < F::QT; ++qt) {
+      w.l[qt] += lsum[qt];
+      w.bad |= lsum[qt] > kOverflowGuard;
     }
   }
-#pragma unroll
-  for (int qt = 0; qt < F::QT; ++qt) {
-    w.l[qt] += lsum[qt];
-    w.bad |= lsum[qt] > kOverflowGuard;
-  }
-}
 
-// One pass over the row's block list with the two-stage copy pipeline: the
-// copies of the next listed block go into one LDS stage while the MFMA work
-// reads the other; one barrier per block.  FIRST_MODE applies to the first
-// listed block, MODE to the rest.
-template <Mode FIRST_MODE, Mode MODE, int D, int BLK>
-__device__ __forceinline__ void run_pass(WaveState<D, BLK>& w, uint32_t lds0, const uint16_t* __restrict__ kh,
-                                         const uint16_t* __restrict__ vh,
-                                         const __attribute__((address_space(4))) int32_t* list, int cnt, int nk,
-                                         int wave, const DmaOffsets<D, BLK>& dma, float scale_log2) {
-  auto next_valid = [&](int t) {
-    while (t < cnt && (unsigned)list[t] >= (unsigned)nk) ++t;
-    return t;
-  };
-  int t = next_valid(0);
-  if (t >= cnt) return;
-  issue_tile<0, D, BLK>(lds0, kh, vh, list[t], wave, dma);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // peeled first block (stage 0), then two blocks per turn (stages 1, 0) so
-  // that every LDS address is a loop-invariant register plus an immediate
-  int tn = next_valid(t + 1);
-  if (tn < cnt) issue_tile<1, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
-  compute_tile<FIRST_MODE, 0, D, BLK>(w, scale_log2);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  t = tn;
-  while (t < cnt) {
-    tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<0, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
-    compute_tile<MODE, 1, D, BLK>(w, scale_log2);
+  // One block that has a successor.  ST: parity of t; jv: block id of t+1
+  // (its V is copied now), jk: block id of t+2 (its K is copied now; past
+  // the end of the list a valid block whose scores are never used).
+  // Issue order (the sched_barrier fences keep it): each score MFMA of block
+  // t+1 is followed by its share of the softmax of block t (NE / NS
+  // elements), every d-step by the K and Q fragment reads kKAhead steps
+  // ahead, and its share of the 2 * SEGS copies (K first: it is needed
+  // first); the last slots also start the V^T reads of the PV product; then
+  // the PV MFMAs of block t with their V^T reads and the row sums.
+  template <int ST>
+  __device__ __forceinline__ void iter(f32x16 (&scur)[F::KTW][F::QT], f32x16 (&snext)[F::KTW][F::QT], int jv,
+                                       int jk) {
+    constexpr int NS = F::DS * F::KTW * F::QT;  // score MFMAs per block
+    constexpr int NE = Softmax<D, BLK>::NE;     // softmax elements per lane and block
+    static_assert(NE % NS == 0 && (NE / NS) % 2 == 0, "softmax share per slot must be whole pairs");
+    constexpr int EPS = NE / NS;
+    constexpr int NC = 2 * F::SEGS;             // copies per wave and block
+    bf16x8 pb[F::PS][F::QT];
+    Softmax<D, BLK> sm = {scur, pb, {}, scale_log2, 0.f};
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) sm.mb[qt] = w.m[qt] * scale_log2;
+    const unsigned char* kb = sl.k[ST ^ 1];
+    // score MFMAs d-step major, m = (s * KTW + kt) * QT + qt: the K and Q
+    // fragments of step s feed KTW * QT MFMAs
+    bf16x8 kf[F::DS][F::KTW], vf[kVAhead + 1];
+    auto read_step = [&](int st) {
+#pragma unroll
+      for (int kt = 0; kt < F::KTW; ++kt) kf[st][kt] = k_fragment<D, BLK>(w, kb, st, kt);
+    };
+#pragma unroll
+    for (int st = 0; st < kKAhead && st < F::DS; ++st) read_step(st);
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+      const int s = m / (F::KTW * F::QT), kt = (m / F::QT) % F::KTW, qt = m % F::QT;
+      if (kt == 0 && qt == 0 && s + kKAhead < F::DS) read_step(s + kKAhead);
+      if (s == 0)
+        mfma_score_first(snext[kt][qt], kf[s][kt], w.qf[qt][s]);
+      else
+        mfma_score(snext[kt][qt], kf[s][kt], w.qf[qt][s]);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c * NS / NC != m) continue;
+        if (c < F::SEGS) {
+          copy_one<0, D, BLK>(cp, sl.k[ST], jk, c);
+        } else {
+          copy_one<1, D, BLK>(cp, sl.v[ST ^ 1], jv, c - F::SEGS);
+        }
+      }
+      if (m == NS - 1) pv_prefetch(vf, sl.v[ST]);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) sm.element(m * EPS + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pv(pb, sl.v[ST], vf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    t = tn;
-    if (t >= cnt) break;
-    tn = next_valid(t + 1);
-    if (tn < cnt) issue_tile<1, D, BLK>(lds0, kh, vh, list[tn], wave, dma);
-    compute_tile<MODE, 0, D, BLK>(w, scale_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    t = tn;
+    // the scores of block t+1 are read by the VALU in the next iteration; the
+    // PV MFMAs issued after them have drained the matrix pipe
+    fence_vgpr<false>(snext);
   }
-}
+
+  // The last listed block: softmax and PV only (every copy has landed, so
+  // the V slot may be a runtime pointer).
+  __device__ __forceinline__ void last(f32x16 (&scur)[F::KTW][F::QT], const unsigned char* vb) {
+    bf16x8 pb[F::PS][F::QT];
+    Softmax<D, BLK> sm = {scur, pb, {}, scale_log2, 0.f};
+#pragma unroll
+    for (int qt = 0; qt < F::QT; ++qt) sm.mb[qt] = w.m[qt] * scale_log2;
+    bf16x8 vf[kVAhead + 1];
+    pv_prefetch(vf, vb);
+#pragma unroll
+    for (int e = 0; e < Softmax<D, BLK>::NE; ++e) sm.element(e);
+    pv(pb, vb, vf);
+    fence_agpr(w.oacc);  // O may be copied between registers after this point
+    __syncthreads();
+  }
+
+  // One pass over the row's listed blocks.  With first the reference
+  // maximum comes from the first listed block; otherwise w.m is given.
+  __device__ __forceinline__ void run(int lane, bool first) {
+    const int nvalid = ls.valid(lane);
+    if (nvalid == 0) return;
+    ls.start(lane);
+    const int j0 = ls.take(lane);
+    int j1 = ls.take(lane), j2 = ls.take(lane);
+    fallback = j0;
+    f32x16 sa[F::KTW][F::QT], sb[F::KTW][F::QT];
+    // block 0: K into slot 0; then its scores while K(1) and V(0) are copied
+    copy_tile<0, D, BLK>(cp, sl.k[0], j0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j1 >= 0) copy_tile<0, D, BLK>(cp, sl.k[1], j1);
+    copy_tile<1, D, BLK>(cp, sl.v[0], j0);
+    scores<D, BLK>(w, sl.k[0], sa);
+    if (first) tile_max<D, BLK>(sa, w.m);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Steady state, two blocks per turn so that slots are compile-time
+    // constants.  Every block but the last computes its successor's scores;
+    // when that count is odd one phantom step past the end keeps the turns
+    // whole (it copies a valid block and its scores are never used), so the
+    // last block always sits in slot 0 and there is a single loop exit.
+    const int steps = nvalid - 1;
+    const bool phantom = steps & 1;
+    // block ids of t+1 and t+2, taken an iteration ahead; past the end of
+    // the list (the phantom step, the K copy for a block that does not
+    // exist) the fallback is copied and never used
+    if (j1 < 0) j1 = fallback;
+    if (j2 < 0) j2 = fallback;
+    for (int turn = 0; turn < (steps + 1) / 2; ++turn) {
+      int j3 = ls.take(lane);
+      iter<0>(sa, sb, j1, j2);
+      j1 = j2;
+      j2 = j3 >= 0 ? j3 : fallback;
+      j3 = ls.take(lane);
+      iter<1>(sb, sa, j1, j2);
+      j1 = j2;
+      j2 = j3 >= 0 ? j3 : fallback;
+    }
+    fence_agpr(w.oacc);
+    if (!phantom) last(sa, sl.v[0]);
+  }
+
+  // Rare path: the true maximum of every query over the listed blocks (no softmax, no V).
+  __device__ __forceinline__ void max_sweep(int lane) {
+    f32x16 sa[F::KTW][F::QT];
+    ls.start(lane);
+    for (int j = ls.take(lane); j >= 0; j = ls.take(lane)) {
+      copy_tile<0, D, BLK>(cp, sl.k[0], j);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      scores<D, BLK>(w, sl.k[0], sa);
+      float mx[F::QT];
+      tile_max<D, BLK>(sa, mx);
+#pragma unroll
+      for (int qt = 0; qt < F::QT; ++qt) w.m[qt] = fmaxf(w.m[qt], mx[qt]);
+      __syncthreads();
+    }
+  }
+};
 
 // Split-KV: with `splits` > 0 workgroup g handles segment g % splits of row
 // g / splits, the list positions [s*cnt/splits, (s+1)*cnt/splits), and
@@ -346,14 +607,17 @@ __device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* 
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
+__global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_fa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   using F = Fa<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[F::LDS_BYTES];
-  const uint32_t lds0 = lds_addr(lds);
+  __shared__ __attribute__((aligned(1024))) unsigned char k_slot0[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_slot1[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_slot0[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_slot1[F::T];
+  const Slots sl = {{k_slot0, k_slot1}, {v_slot0, v_slot1}};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -366,30 +630,37 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
   const size_t N = (size_t)nk * BLK;
   const uint16_t* kh = k + (size_t)bh * N * D;
   const uint16_t* vh = v + (size_t)bh * N * D;
-  // The list is read-only here and wave-uniform: scalar loads via the constant address space.
-  const __attribute__((address_space(4))) int32_t* list =
-      (const __attribute__((address_space(4))) int32_t*)(kv_idx + (size_t)row * top_k + sg.begin);
-  const int cnt = sg.count;
+  ListStream ls;
+  ls.list = kv_idx + (size_t)row * top_k + sg.begin;
+  ls.cnt = sg.count;
+  ls.nk = nk;
 
   WaveState<D, BLK> w;
   const size_t qrow0 = (size_t)bh * nq * BLK + (size_t)iq * BLK + qg * F::QW;
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) {
+    // B operand of S^T = K Q^T: lane l holds query 32qt + l%32 of this wave's
+    // group, d = 16s + 8(l/32) + 0..7
     const uint4* qrow = reinterpret_cast<const uint4*>(q + (qrow0 + 32 * qt + qc) * D);
 #pragma unroll
-    for (int s = 0; s < F::DS; ++s) w.qf[qt][s] = as_bf16x8(qrow[2 * s + hh]);
+    for (int s = 0; s < F::DS; ++s) {
+      const uint4 u = qrow[2 * s + hh];
+      __builtin_memcpy(&w.qf[qt][s], &u, 16);
+      asm volatile("" : "+a"(w.qf[qt][s]));  // Q lives in AGPRs
+    }
     w.m[qt] = -__builtin_inff();
     w.l[qt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < F::DT; ++dt)
+    for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
+      asm volatile("" : "+a"(w.oacc[dt][qt]));  // O lives in AGPRs
+    }
   }
-
 #pragma unroll
   for (int s = 0; s < F::DS; ++s) {
     const int r = kbase + qc;
-    w.ko[s] = lds0 + (uint32_t)(r * F::NCH + ((2 * s + hh) ^ F::swz_k(r))) * 16u;
+    w.ko[s] = (uint32_t)(r * F::NCH + ((2 * s + hh) ^ F::swz_k(r))) * 16u;
   }
   {
     const int grp = lane >> 4, j = lane & 15;
@@ -399,14 +670,26 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < F::DT; ++dt) {
       const int c = (4 * dt + 2 * gd + ((j & 3) >> 1)) ^ vsw;
-      w.vo[dt] = lds0 + F::V0 + (uint32_t)(key0 * F::NCH * 16 + 8 * (j & 1) + c * 16);
+      w.vo[dt] = (uint32_t)(key0 * F::NCH * 16 + 8 * (j & 1) + c * 16);
     }
   }
-  DmaOffsets<D, BLK> dma;
-  dma.init(wave, lane);
+  Copier<D, BLK> cp;
+  cp.init(kh, vh, (uint32_t)(N * D * 2), wave, lane);
   w.bad = false;
-  run_pass<Mode::First, Mode::Normal, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
-  if (__syncthreads_or(w.bad)) {
+  Pass<D, BLK> pass = {w, sl, ls, cp, scale_log2, 0};
+  for (bool first = true;; first = false) {
+    pass.run(lane, first);
+    if (!first) break;
+    // Did any lane of any wave see an overflow?  One flag per wave in a free
+    // slot (every copy has landed and every wave has passed the last barrier).
+    int* flags = reinterpret_cast<int*>(v_slot0);
+    if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(w.bad) != 0;
+    __syncthreads();
+    int any_bad = 0;
+#pragma unroll
+    for (int i = 0; i < F::NW; ++i) any_bad |= flags[i];
+    __syncthreads();
+    if (!any_bad) break;
     // Rare: some logit exceeded the first block's maximum by more than 40
     // log2-units.  Find each query's true maximum, then redo the row at it.
 #pragma unroll
@@ -414,17 +697,27 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
       w.m[qt] = -__builtin_inff();
       w.l[qt] = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < F::DT; ++dt)
+      for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) w.oacc[dt][qt][r] = 0.f;
+        asm volatile("" : "+a"(w.oacc[dt][qt]));
+      }
     }
-    run_pass<Mode::MaxOnly, Mode::MaxOnly, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
-    run_pass<Mode::Normal, Mode::Normal, D, BLK>(w, lds0, kh, vh, list, cnt, nk, wave, dma, scale_log2);
+    pass.max_sweep(lane);
   }
+  __syncthreads();
+  fence_agpr(w.oacc);  // the last PV MFMAs have written O before it is read
 
-  // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0 through LDS.
-  float* xo = reinterpret_cast<float*>(lds);           // [qg][dt][qt][r][lane]: blk*d floats = both K stages
-  float* xm = reinterpret_cast<float*>(lds + F::V0);  // m: [qg][qt][lane], then l: [qg][qt][lane]
+  // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0
+  // through LDS.  O of the kg = 1 waves fills both K slots exactly
+  // (NQG * DT * QT * 16 registers of 64 lanes = 2 * BLK * D * 2 bytes).
+  constexpr int HALF = F::NQG * F::DT * F::QT * 16 / 2;  // register slots per K slot
+  float* xm = reinterpret_cast<float*>(v_slot0);        // m: [qg][qt][lane], then l: [qg][qt][lane]
+  auto xo_at = [&](int dt, int qt, int r) -> float* {
+    const int f = ((qg * F::DT + dt) * F::QT + qt) * 16 + r;
+    return f < HALF ? reinterpret_cast<float*>(k_slot0) + f * 64 + lane
+                    : reinterpret_cast<float*>(k_slot1) + (f - HALF) * 64 + lane;
+  };
   float lw[F::QT];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) lw[qt] = w.l[qt] + __shfl_xor(w.l[qt], 32);
@@ -436,7 +729,7 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < F::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[(((qg * F::DT + dt) * F::QT + qt) * 16 + r) * 64 + lane] = w.oacc[dt][qt][r];
+        for (int r = 0; r < 16; ++r) *xo_at(dt, qt, r) = w.oacc[dt][qt][r];
     }
   }
   __syncthreads();
@@ -464,8 +757,7 @@ __global__ __launch_bounds__(512) void sparse_fa_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
-            const float o1 = xo[(((qg * F::DT + dt) * F::QT + qt) * 16 + r) * 64 + lane];
-            o[e] = (w.oacc[dt][qt][r] * a0 + o1 * a1) * inv;
+            o[e] = (w.oacc[dt][qt][r] * a0 + *xo_at(dt, qt, r) * a1) * inv;
           }
           if (splits) {
             *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * hh) = make_float4(o[0], o[1], o[2], o[3]);
