@@ -31,7 +31,6 @@ def parse():
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the keep-all comparison")
-    ap.add_argument("--cpu-tokens", type=int, default=32768, help="query tokens in the oracle's attention sample")
     ap.add_argument("--cold-reps", type=int, default=20, help="layers timed after a 1 GiB cache-flushing write")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (reference for HBM counter scaling)")
@@ -225,7 +224,7 @@ def main():
     res["split_kv_small"] = bench_split_small(velox, stream)
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(cfg, x, gi, cnt)
     print(json.dumps(res), flush=True)
 
 
@@ -378,40 +377,68 @@ def bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el
                     "once-per-chunk velox_pool_keys cost of appending a finished chunk"}
 
 
-def cpu_baseline(cfg, x, gi, cnt, n_tokens):
-    """The oracle (fp64, OpenMP) on this host: full routing plus attention for a
-    sample of query tokens, scaled to the whole layer."""
-    import platform
-
-    import numpy as np
-
-    from oracle import velox_oracle as O
-
-    t0 = time.perf_counter()
-    O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
-    t_route = time.perf_counter() - t0
-    total = cfg.batch * cfg.heads * cfg.chunk_tokens
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(total, size=min(n_tokens, total), replace=False)).astype(np.int64)
-    t0 = time.perf_counter()
-    O.attn(x.q, x.k, x.v, gi, cnt, cfg.block, tokens=toks)
-    t_attn = time.perf_counter() - t0
-    t_layer = t_route + t_attn * total / toks.size
-    f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
-    model = platform.processor() or ""
+def cpu_model_name():
+    """lscpu's model name (falls back to /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(f_exec / t_layer / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
-            "kind": "oracle", "ms_per_layer": round(t_layer * 1e3, 1), "route_s": round(t_route, 3),
-            "attn_sample_s": round(t_attn, 3), "cpu_model": model,
-            "sample": f"full routing of all {cfg.rows} rows + fp64 attention of {toks.size} of {total} query "
-                      f"tokens (seeded uniform sample) on the same inputs and GPU block lists, attention time "
-                      f"scaled by {total / toks.size:.1f}"}
+    return ""
+
+
+def oracle_layer_seconds(O, cfg, x, kv_idx=None, kv_cnt=None):
+    """Wall time of the oracle's whole layer: routing of every row, then fp64
+    attention of every query token over the given lists (the oracle's own if None)."""
+    t0 = time.perf_counter()
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    t_route = time.perf_counter() - t0
+    if kv_idx is None:
+        kv_idx, kv_cnt = r["kv_idx"], r["kv_cnt"]
+    t0 = time.perf_counter()
+    O.attn(x.q, x.k, x.v, kv_idx, kv_cnt, cfg.block)
+    return t_route, time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, x, gi, cnt):
+    """The oracle (fp64, OpenMP) on this host, unsampled: routing of every row plus
+    attention of every query token of the workload over the GPU's block lists,
+    then the Tiny and Small workloads on one thread."""
+    from oracle import velox_oracle as O
+    from synth import get_config, make_inputs
+
+    threads = O.num_threads()
+    t_route, t_attn = oracle_layer_seconds(O, cfg, x, gi, cnt)
+    t_layer = t_route + t_attn
+    f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(cnt.sum())
+    single = {}
+    O.set_threads(1)
+    try:
+        for name in ("tiny", "small"):
+            c = get_config(name)
+            xs = make_inputs(c)
+            tr, ta = oracle_layer_seconds(O, c, xs)
+            single[name] = {"ms_per_layer": round((tr + ta) * 1e3, 1), "route_ms": round(tr * 1e3, 1),
+                            "attn_ms": round(ta * 1e3, 1)}
+    finally:
+        O.set_threads(threads)
+    total = cfg.batch * cfg.heads * cfg.chunk_tokens
+    return {"value": round(f_exec / t_layer / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sampled": False, "ms_per_layer": round(t_layer * 1e3, 1),
+            "route_s": round(t_route, 3), "attn_s": round(t_attn, 3), "cpu_model": cpu_model_name(),
+            "single_thread": single,
+            "sample": f"unsampled: routing of all {cfg.rows} rows and fp64 attention of all {total} query "
+                      f"tokens over the GPU's block lists, {threads} OpenMP threads; Tiny and Small whole "
+                      f"layers (oracle routing and attention) on one thread"}
 
 
 if __name__ == "__main__":

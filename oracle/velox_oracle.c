@@ -71,6 +71,16 @@ int velox_oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count for the following calls (n >= 1); no effect on the results,
+ * every parallel loop writes disjoint outputs. */
+void velox_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Mean of each group of `blk` consecutive rows of x, viewed as
  * [nblocks * blk, d].  out: [nblocks, d]. */
 int velox_oracle_pool(const void *x, int dtype, int64_t nblocks, int blk, int d, double *out) {

@@ -31,6 +31,8 @@ def lib():
             build_oracle()
         L = C.CDLL(_LIB_PATH)
         L.velox_oracle_num_threads.restype = _I
+        L.velox_oracle_set_threads.argtypes = [_I]
+        L.velox_oracle_set_threads.restype = None
         L.velox_oracle_pool.argtypes = [_P, _I, _L, _I, _I, _P]
         L.velox_oracle_scores.argtypes = [_P, _P, _L, _I, _I, _I, _P]
         L.velox_oracle_modulate.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _P]
@@ -49,6 +51,11 @@ def lib():
 
 def num_threads() -> int:
     return lib().velox_oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls (timing only; results do not depend on it)."""
+    lib().velox_oracle_set_threads(int(n))
 
 
 def _ptr(a: Optional[np.ndarray]):

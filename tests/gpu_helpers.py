@@ -1,5 +1,5 @@
-"""Shared helpers for the GPU tests: device upload of synthetic inputs and
-sampling of rows/tokens for full-size checks."""
+"""Shared helpers for the GPU tests: device upload of synthetic inputs and the
+query tokens that full-size checks compare."""
 from __future__ import annotations
 
 import functools
@@ -42,17 +42,19 @@ def cached_inputs(name: str):
     return make_inputs(cfg)
 
 
-def sample_tokens(cfg, n_rows: int, per_row: int, seed: int = 0):
-    """Flat token indices (b*H + h)*T + t over a spread of rows, always including
-    the first and last row and the first and last token of a block."""
+def every_row_tokens(cfg, per_row: int = 8, seed: int = 0):
+    """Flat token indices covering every row: in each query block the first and
+    last query of every 32-query MFMA tile (t = 32g and 32g + 31, which includes
+    the block's first and last token and both halves of each 64-query wave
+    group), topped up with random queries to `per_row` per block."""
     rng = np.random.default_rng(seed)
-    rows = cfg.rows
-    pick = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, size=min(n_rows, rows), replace=False)]))
+    blk = cfg.block
+    fixed = np.array(sorted({32 * g + e for g in range(blk // 32) for e in (0, 31)}), np.int64)
+    rest = np.setdiff1d(np.arange(blk), fixed)
     toks = []
-    for r in pick:
-        bh, i = divmod(int(r), cfg.nq)
-        base = bh * cfg.chunk_tokens + i * cfg.block
-        inner = rng.choice(cfg.block, size=min(per_row, cfg.block), replace=False)
-        for t in np.unique(np.concatenate([[0, cfg.block - 1], inner])):
-            toks.append(base + int(t))
-    return np.array(sorted(toks), np.int64), pick
+    for r in range(cfg.rows):
+        bh, i = divmod(r, cfg.nq)
+        base = bh * cfg.chunk_tokens + i * blk
+        extra = rng.choice(rest, size=max(0, per_row - fixed.size), replace=False)
+        toks.append(base + np.union1d(fixed, extra))
+    return np.concatenate(toks).astype(np.int64)

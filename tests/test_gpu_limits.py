@@ -2,10 +2,10 @@
 chunk, VELOX_MAX_KV_BLOCKS = 8192 KV blocks), against the oracle.
 
 * d = 64 / blk = 64: T = 4096 (64 query blocks), 127 past chunks (nk = 8192): routing
-  with top-k 1000 under the gap rule, attention of sampled tokens over the oracle's
-  lists, and keep-all (lists of 8192 blocks) against the oracle.
+  with top-k 1000 under the gap rule, attention over the oracle's lists (every row,
+  8 queries per block), and keep-all (lists of 8192 blocks) against the oracle.
 * d = 128 / blk = 128 at 64 query blocks (T = 8192) with 31 past chunks (nk = 2048):
-  routing and sampled attention.
+  routing and attention (every row, 8 queries per block).
 Same bars as the workload parity tests.
 """
 import numpy as np
@@ -17,7 +17,7 @@ import geometry_routed_block_velox_amd as velox
 from oracle import velox_oracle as O
 from synth import make_inputs
 from synth.configs import Config
-from tests.gpu_helpers import dev_inputs, out_to_f64, sample_tokens, say, to_dev
+from tests.gpu_helpers import dev_inputs, every_row_tokens, out_to_f64, say, to_dev
 from tests.parity_rules import BF16_MAX_ABS, BF16_MEAN_ABS, check_close, check_selection
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,7 @@ def test_route_and_attention_at_the_limits(cfg):
     st = check_selection(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), r["m"], r["kth"], r["kv_idx"], cfg.k_eff,
                          cfg.nk - cfg.ncur)
     say(f"{cfg.name}: selection {st}")
-    toks, _ = sample_tokens(cfg, n_rows=8, per_row=3, seed=5)
+    toks = every_row_tokens(cfg, seed=5)
     out = velox.sparse_attn(d["q"], d["k"], d["v"], to_dev(r["kv_idx"]), to_dev(r["kv_cnt"]), cfg.block)
     torch.cuda.synchronize()
     ref, _ = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block, tokens=toks)

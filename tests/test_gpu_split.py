@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 import geometry_routed_block_velox_amd as velox
 from oracle import velox_oracle as O
-from tests.gpu_helpers import cached_inputs, dev_inputs, out_to_f64, sample_tokens, say, to_dev
+from tests.gpu_helpers import cached_inputs, dev_inputs, every_row_tokens, out_to_f64, say, to_dev
 from tests.parity_rules import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, check_close
 
 pytestmark = pytest.mark.gpu
@@ -66,16 +66,15 @@ def test_split_matches_oracle(name, splits):
     r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
     toks = None
     if cfg.rows > 64:
-        toks, _ = sample_tokens(cfg, n_rows=24, per_row=6, seed=3)
+        toks = every_row_tokens(cfg, seed=3)
     compare(x, r["kv_idx"], r["kv_cnt"], splits, toks)
 
 
-def test_split_headline_sampled():
+def test_split_headline_every_row():
     x = cached_inputs("headline")
     cfg = x.cfg
     r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
-    toks, _ = sample_tokens(cfg, n_rows=12, per_row=4, seed=4)
-    compare(x, r["kv_idx"], r["kv_cnt"], 2, toks)
+    compare(x, r["kv_idx"], r["kv_cnt"], 2, every_row_tokens(cfg, seed=4))
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
