@@ -25,7 +25,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "VeloxError", "Problem", "Status", "lib", "library_path", "velox_check", "velox_route_workspace_bytes",
-    "route", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits", "score",
+    "route", "route_noalloc", "select", "sparse_attn", "problem_for", "pool_keys", "route_cached", "auto_splits", "score",
     "frustum_overlap",
 ]
 
@@ -88,6 +88,8 @@ def lib():
         L.velox_route_workspace_bytes.restype = C.c_size_t
         L.velox_route.argtypes = [P, V, V, V, V, V, V, V, V, C.c_size_t, V]
         L.velox_route.restype = C.c_int
+        L.velox_route_noalloc.argtypes = [P, V, V, V, V, V, V, V, V]
+        L.velox_route_noalloc.restype = C.c_int
         L.velox_score.argtypes = [P, V, V, V, V, C.c_size_t, V]
         L.velox_score.restype = C.c_int
         L.velox_frustum_overlap.argtypes = [P, V, V, V, C.c_float, V, V, V]
@@ -230,6 +232,39 @@ def route(q, k, overlap, covered, block: int, top_k: int, alpha: float, return_s
                            _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(st, "velox_route")
     return (kv_idx, kv_cnt, scores) if return_scores else (kv_idx, kv_cnt)
+
+
+def route_noalloc(q, k, overlap, covered, block: int, top_k: int, alpha: float, out, scores=None, stream=None,
+                  modulation: int = MOD_SCALE):
+    """velox_route_noalloc: velox_route with the library's per-GPU scratch array as its
+    workspace.  The caller passes the outputs: out = (kv_idx [B,H,nq,top_k] int32,
+    kv_cnt [B,H,nq] int32), and optionally scores [B,H,nq,nk] float32; nothing is
+    allocated.  Calls that overlap on one GPU race on the scratch array."""
+    torch = _torch()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, ndim=4)
+    p = problem_for(tuple(q.shape), k.shape[2], block, top_k, alpha, _dtype_code(q), modulation)
+    _raise(velox_check(p), "velox_route_noalloc")
+    B, H, T, d = q.shape
+    if tuple(k.shape) != (B, H, k.shape[2], d):
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if p.past_chunks > 0:
+        _dev(overlap, "overlap", torch.float32)
+        if tuple(overlap.shape) != (B, p.nq, p.past_chunks):
+            raise ValueError(f"overlap must be [{B},{p.nq},{p.past_chunks}], got {tuple(overlap.shape)}")
+    else:
+        overlap = None
+    _dev(covered, "covered", torch.uint8)
+    if tuple(covered.shape) != (B, p.nq):
+        raise ValueError(f"covered must be [{B},{p.nq}], got {tuple(covered.shape)}")
+    kv_idx = _out(out[0], "kv_idx", (B, H, p.nq, top_k), torch.int32)
+    kv_cnt = _out(out[1], "kv_cnt", (B, H, p.nq), torch.int32)
+    if scores is not None:
+        scores = _out(scores, "scores", (B, H, p.nq, p.nk), torch.float32)
+    st = lib().velox_route_noalloc(C.byref(p), _ptr(q), _ptr(k), _ptr(overlap), _ptr(covered), _ptr(kv_idx),
+                                   _ptr(kv_cnt), _ptr(scores), _stream(stream))
+    _raise(st, "velox_route_noalloc")
+    return kv_idx, kv_cnt
 
 
 def score(q, k, block: int, scores=None, workspace=None, stream=None):

@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "libvelox.so")
 # Host-only C++ (g++: argument checks and the launching entry points) and HIP
 # kernels (hipcc for gfx950).
 HOST_SOURCES = ["velox_check.cpp", "velox_api.cpp"]
-HIP_SOURCES = ["block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip"]
+HIP_SOURCES = ["block_score.hip", "modulate_select.hip", "sparse_fa.hip", "frustum.hip", "scratch.hip"]
 SOURCES = HOST_SOURCES + HIP_SOURCES
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")

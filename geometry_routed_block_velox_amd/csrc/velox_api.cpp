@@ -22,9 +22,7 @@ hipStream_t hip_stream(velox_stream_t s) { return reinterpret_cast<hipStream_t>(
 // Scores buffer of the routing calls: the caller's, or the workspace past the pooled queries.
 float* scores_buffer(const velox_problem* p, float* scores, void* workspace) {
   if (scores) return scores;
-  const velox::Dims x = velox::dims(*p);
-  const size_t rows = (size_t)x.B * x.H * x.nq;
-  return reinterpret_cast<float*>(static_cast<char*>(workspace) + velox::align256(rows * x.d * sizeof(float)));
+  return reinterpret_cast<float*>(static_cast<char*>(workspace) + velox::route_qbar_bytes(*p));
 }
 
 }  // namespace
@@ -40,6 +38,24 @@ velox_status velox_route(const velox_problem* p, const void* q, const void* k, c
   float* s = scores_buffer(p, scores, workspace);
   hipStream_t hs = hip_stream(stream);
   hipError_t e = velox::launch_pool_queries(*p, q, qbar, hs);
+  if (e == hipSuccess) e = velox::launch_block_score(*p, k, qbar, s, hs);
+  if (e == hipSuccess) e = velox::launch_modulate_select(*p, s, overlap, covered, kv_idx, kv_cnt, hs);
+  return hip_status(e);
+}
+
+velox_status velox_route_noalloc(const velox_problem* p, const void* q, const void* k, const float* overlap,
+                                 const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, float* scores,
+                                 velox_stream_t stream) {
+  const velox_status st = velox::check_route_noalloc(p, q, k, overlap, covered, kv_idx, kv_cnt, scores);
+  if (st != VELOX_OK) return st;
+  void* scratch = nullptr;
+  hipError_t e = velox::device_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  // the same layout as velox_route's workspace: pooled queries, then the scores
+  float* qbar = static_cast<float*>(scratch);
+  float* s = scores_buffer(p, scores, scratch);
+  hipStream_t hs = hip_stream(stream);
+  e = velox::launch_pool_queries(*p, q, qbar, hs);
   if (e == hipSuccess) e = velox::launch_block_score(*p, k, qbar, s, hs);
   if (e == hipSuccess) e = velox::launch_modulate_select(*p, s, overlap, covered, kv_idx, kv_cnt, hs);
   return hip_status(e);

@@ -51,6 +51,23 @@ velox_status check_route(const velox_problem* p, const void* q, const void* k, c
   return check_workspace(workspace, workspace_bytes, velox_route_workspace_bytes(p));
 }
 
+size_t route_qbar_bytes(const velox_problem& p) {
+  const Dims x = dims(p);
+  return align256((size_t)x.B * x.H * x.nq * x.d * sizeof(float));
+}
+
+velox_status check_route_noalloc(const velox_problem* p, const void* q, const void* k, const float* overlap,
+                                 const uint8_t* covered, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                 const float* scores) {
+  const velox_status st = check_problem(p, true);
+  if (st != VELOX_OK) return st;
+  if (!q || !k || !covered || !kv_idx || !kv_cnt || (p->past_chunks > 0 && !overlap)) return VELOX_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k)) return VELOX_ERR_MISALIGNED;
+  const size_t need = scores ? route_qbar_bytes(*p) : velox_route_workspace_bytes(p);
+  if (need > VELOX_NOALLOC_SCRATCH_BYTES) return VELOX_ERR_WORKSPACE;
+  return VELOX_OK;
+}
+
 velox_status check_score(const velox_problem* p, const void* q, const void* k, const float* scores,
                          const void* workspace, size_t workspace_bytes) {
   const velox_status st = check_problem(p, true);

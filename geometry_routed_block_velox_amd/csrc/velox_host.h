@@ -46,6 +46,14 @@ velox_status check_problem(const velox_problem* p, bool routing);
 velox_status check_route(const velox_problem* p, const void* q, const void* k, const float* overlap,
                          const uint8_t* covered, const int32_t* kv_idx, const int32_t* kv_cnt, const void* workspace,
                          size_t workspace_bytes);
+// velox_route_noalloc: velox_route's checks without the workspace, and the
+// scratch it needs (pooled queries, plus the scores when `scores` is NULL)
+// within VELOX_NOALLOC_SCRATCH_BYTES.
+velox_status check_route_noalloc(const velox_problem* p, const void* q, const void* k, const float* overlap,
+                                 const uint8_t* covered, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                 const float* scores);
+// Bytes of the pooled queries, the first part of a routing workspace.
+size_t route_qbar_bytes(const velox_problem& p);
 velox_status check_score(const velox_problem* p, const void* q, const void* k, const float* scores,
                          const void* workspace, size_t workspace_bytes);
 velox_status check_frustum_overlap(const velox_problem* p, const float* yaw, const float* past_depth,

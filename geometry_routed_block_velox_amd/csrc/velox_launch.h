@@ -23,6 +23,10 @@ hipError_t launch_frustum_overlap(const velox_problem& p, const float* yaw, cons
                                   hipStream_t s);
 hipError_t launch_modulate_select(const velox_problem& p, const float* scores, const float* overlap,
                                   const uint8_t* covered, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
+// This device's scratch array of VELOX_NOALLOC_SCRATCH_BYTES (a static
+// __device__ array): its address on the current device, looked up there on
+// the first call and kept per device.  Allocates nothing.
+hipError_t device_scratch(void** ptr);
 // splits == 0: one workgroup per row, direct output.  splits > 0: split-KV with
 // float32 partials part_o [rows*splits, blk, d] and part_lse [rows*splits, blk].
 hipError_t launch_sparse_attn(const velox_problem& p, const void* q, const void* k, const void* v,

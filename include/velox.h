@@ -133,6 +133,24 @@ velox_status velox_route(const velox_problem *p, const void *q, const void *k, c
                          const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, float *scores,
                          void *workspace, size_t workspace_bytes, velox_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): velox_route
+ * with its workspace taken from a scratch array the library holds per GPU
+ * (VELOX_NOALLOC_SCRATCH_BYTES, held by each GPU the call runs on until the
+ * process ends).  Arguments and results as velox_route, without `workspace`;
+ * the same kernels run, so kv_idx, kv_cnt and scores are identical to
+ * velox_route's.  The call allocates nothing (no hipMalloc or hipFree); its
+ * first call on a device looks the array's address up there.
+ * Errors: velox_route's, and VELOX_ERR_WORKSPACE when the pooled queries plus,
+ * if `scores` is NULL, the score matrix exceed VELOX_NOALLOC_SCRATCH_BYTES
+ * (checked before any device work).  The array is shared by every call on one
+ * GPU and keeps the last call's contents (every byte a call reads it wrote
+ * first): calls that overlap on one GPU, e.g. on two streams, race. */
+#define VELOX_NOALLOC_SCRATCH_BYTES (24u << 20)
+velox_status velox_route_noalloc(const velox_problem *p, const void *q, const void *k, const float *overlap,
+                                 const uint8_t *covered, int32_t *kv_idx, int32_t *kv_cnt, float *scores,
+                                 velox_stream_t stream);
+
 /* The scoring step of velox_route alone: writes the raw importance
  * s [B,H,nq,nk] float32 (same values as velox_route's `scores`) for a later
  * velox_select.  Lets a caller build the overlap concurrently (below) and

@@ -24,6 +24,10 @@ hipError_t launch_modulate_select(const velox_problem&, const float*, const floa
                                   int32_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t device_scratch(void** ptr) {
+  *ptr = nullptr;
+  return hipErrorNoDevice;
+}
 hipError_t launch_sparse_attn(const velox_problem&, const void*, const void*, const void*, const int32_t*,
                               const int32_t*, void*, float*, int, float*, float*, hipStream_t) {
   return hipErrorNoDevice;

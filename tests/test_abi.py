@@ -190,3 +190,27 @@ def test_status_strings():
     for s in range(7):
         assert L.velox_status_string(s)
     assert L.velox_status_string(99) == b"unknown status"
+
+
+def test_route_noalloc_validates_before_device_work():
+    """Every check of velox_route_noalloc runs on the host before the scratch array is
+    looked up, so these calls need no GPU."""
+    L = velox.lib()
+    fake = C.c_void_p(0x100000)
+    p = headline()
+    args = (fake, fake, fake, fake, fake, fake, None, None)
+    assert L.velox_route_noalloc(None, *args) == Status.NULL_POINTER
+    assert L.velox_route_noalloc(C.byref(p), None, fake, fake, fake, fake, fake, None, None) == Status.NULL_POINTER
+    assert L.velox_route_noalloc(C.byref(p), fake, fake, fake, fake, fake, None, None, None) == Status.NULL_POINTER
+    assert L.velox_route_noalloc(C.byref(p), C.c_void_p(0x100002), fake, fake, fake, fake, fake, None,
+                                 None) == Status.MISALIGNED
+    bad = headline()
+    bad.top_k = 3
+    assert L.velox_route_noalloc(C.byref(bad), *args) == Status.BAD_SHAPE
+    # 12 heads x 64 query blocks x 8192 KV blocks: the score matrix (25.2 MB) exceeds the
+    # 24 MiB scratch array; with the scores returned only the pooled queries are needed
+    big = Problem(1, 12, 64, 4096, 127, 64, 64, 2.0, velox.VELOX_BF16)
+    assert velox.velox_check(big) == Status.OK
+    assert velox.velox_route_workspace_bytes(big) > (24 << 20)
+    assert L.velox_route_noalloc(C.byref(big), *args) == Status.WORKSPACE
+    assert L.velox_last_hip_error() == 0
