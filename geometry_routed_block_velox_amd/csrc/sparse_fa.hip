@@ -30,10 +30,13 @@
 //    operand is read from the row-major V tile with the LDS transpose read
 //    ds_read_b64_tr_b16, whose 16-lane groups return lane i four consecutive
 //    rows of column i -- exactly the accumulator's key order.
-//  * K and V tiles go from HBM straight to LDS (global_load_lds_dwordx4, no
-//    register staging) into two K and two V slots, separate LDS arrays so
-//    that the compiler's wait counting knows a copy into one slot does not
-//    feed reads of another.  Iteration t copies K of block t+2 and V of block
+//  * The row's Q fragments (the B operand of the score MFMAs) are loaded once
+//    into AGPRs beside the O^T accumulators, so the block loop reads only K
+//    and V from LDS.
+//  * K and V tiles go from HBM straight to LDS (buffer_load_dwordx4 ... lds
+//    through the compiler's builtin, no register staging) into two K and two
+//    V slots, separate LDS arrays so that the compiler's wait counting knows
+//    a copy into one slot does not feed reads of another.  Iteration t copies K of block t+2 and V of block
 //    t+1 while it reads K of block t+1 and V of block t: one barrier per
 //    block, and a copy has a whole iteration to land.  16-byte chunks are
 //    XOR-swizzled per row so that the MFMA operand reads of K and the
@@ -51,6 +54,9 @@
 //    probability sum exceeds 2^40 (logits more than 40 log2-units above the
 //    first block's maximum), the workgroup reruns the row: a max-only sweep
 //    finds the true maximum, then a second pass uses it (all P <= 1).
+//  * The block list is read through a 64-entry window in one VGPR (v_readlane
+//    with a wave-uniform mask of valid entries), so no scalar memory load is
+//    outstanding in the loop to force every LDS wait to drain completely.
 //  * Workgroups are remapped so that the rows of one head run on one XCD and
 //    share its L2 while they walk their ascending block lists.
 // float32 kernel (sparse_fa_f32_kernel): one thread per query token, plain
@@ -69,7 +75,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
-// d-steps by which the K and Q fragment reads run ahead of their score MFMAs.
+// d-steps by which the K fragment reads run ahead of their score MFMAs.
 constexpr int kKAhead = 2;
 // PV steps by which the V^T fragment reads run ahead of their MFMAs.
 constexpr int kVAhead = 6;
@@ -449,7 +455,7 @@ struct Pass {
   // the end of the list a valid block whose scores are never used).
   // Issue order (the sched_barrier fences keep it): each score MFMA of block
   // t+1 is followed by its share of the softmax of block t (NE / NS
-  // elements), every d-step by the K and Q fragment reads kKAhead steps
+  // elements), every d-step by the K fragment reads kKAhead steps
   // ahead, and its share of the 2 * SEGS copies (K first: it is needed
   // first); the last slots also start the V^T reads of the PV product; then
   // the PV MFMAs of block t with their V^T reads and the row sums.
@@ -466,8 +472,8 @@ struct Pass {
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) sm.mb[qt] = w.m[qt] * scale_log2;
     const unsigned char* kb = sl.k[ST ^ 1];
-    // score MFMAs d-step major, m = (s * KTW + kt) * QT + qt: the K and Q
-    // fragments of step s feed KTW * QT MFMAs
+    // score MFMAs d-step major, m = (s * KTW + kt) * QT + qt: the K
+    // fragments of step s feed QT MFMAs each
     bf16x8 kf[F::DS][F::KTW], vf[kVAhead + 1];
     auto read_step = [&](int st) {
 #pragma unroll
