@@ -41,19 +41,33 @@
 //    block, and a copy has a whole iteration to land.  16-byte chunks are
 //    XOR-swizzled per row so that the MFMA operand reads of K and the
 //    transpose reads of V spread over the banks.
-//  * exp2 with log2(e)/sqrt(d) folded into one FMA (hardware v_exp_f32).
-//    Each wave fixes its softmax reference maximum m_ref per query from the
-//    first listed block (the exact maximum over that block, so the largest
-//    probability is >= 1 and nothing underflows) and never rescales O inside
-//    the loop: later probabilities exp2((s - m_ref) c) may exceed 1, which
-//    float32 sums and bf16 P (same exponent range as float32) hold with the
-//    same relative precision, and the final normalisation uses the same
-//    m_ref, so the result is the same softmax.  The probability sums add the
-//    bf16-rounded P that the PV product uses (v_dot2_f32_bf16 against ones),
-//    so numerator and denominator carry the same weights.  If any block's
-//    probability sum exceeds 2^40 (logits more than 40 log2-units above the
-//    first block's maximum), the workgroup reruns the row: a max-only sweep
-//    finds the true maximum, then a second pass uses it (all P <= 1).
+//  * Softmax without rescaling O: the probabilities of a row share one fixed
+//    reference, so O and the probability sums just accumulate, and the final
+//    normalisation divides by a sum taken with the same reference, which
+//    gives the same softmax.  Probabilities above 1 are fine (float32 sums
+//    and bf16 P have float32's exponent range and keep their relative
+//    precision).  The probability sums add the bf16-rounded P that the PV
+//    product uses (v_dot2_f32_bf16 against ones), so numerator and
+//    denominator carry the same weights.  Two passes (attend_row):
+//    - fast pass, tried first: the row's Q is multiplied by log2(e)/sqrt(d)
+//      once, in bf16, so a score is already a base-2 exponent, and the
+//      probability is exp2(s) itself (hardware v_exp_f32, no reference
+//      subtracted, one vector operation per score less than the general
+//      pass).  The pass is taken only while that cannot overflow or
+//      underflow: every query's maximum over the first listed block within
+//      +-40 and every block's probability sum below 2^56; otherwise the
+//      workgroup drops it and runs the general pass.  Rounding the scaled Q
+//      to bf16 perturbs a score by at most 2^-9 c sum_d |q_d k_d| (c the
+//      scale), which moves the row's LSE by at most that much too.
+//    - general pass (a function of its own, so that its registers do not
+//      constrain the fast one): unscaled Q, exp2 with the scale folded into
+//      one FMA, and each wave's reference maximum m_ref per query taken
+//      from the first listed block (the exact maximum over that block, so
+//      the largest probability is >= 1 and nothing underflows).  If any
+//      block's probability sum exceeds 2^40 (logits more than 40 log2-units
+//      above the first block's maximum), the workgroup reruns the row: a
+//      max-only sweep finds the true maximum, then a second pass uses it
+//      (all P <= 1).
 //  * The block list is read through a 64-entry window in one VGPR (v_readlane
 //    with a wave-uniform mask of valid entries), so no scalar memory load is
 //    outstanding in the loop to force every LDS wait to drain completely.
@@ -82,6 +96,11 @@ constexpr int kVAhead = 6;
 
 // Per-block probability sum above which a row is recomputed at its true maximum.
 constexpr float kOverflowGuard = 1099511627776.0f;  // 2^40
+// Fast pass: every query's maximum over the first listed block must lie in
+// [-kFastRange, kFastRange] (log2 units) and every block's probability sum
+// below kFastGuard; otherwise the row is redone by the general pass.
+constexpr float kFastRange = 40.0f;
+constexpr float kFastGuard = 72057594037927936.0f;  // 2^56
 
 template <int D, int BLK>
 struct Fa {
@@ -318,7 +337,7 @@ __device__ __forceinline__ void tile_max(const f32x16 (&sacc)[Fa<D, BLK>::KTW][F
 // Softmax element e of a score tile: query tile qt, 16-key step ps, register
 // i of that step, e = (qt * PS + ps) * 8 + i.  pb[ps][qt] holds keys 16ps.. of
 // the tile, i.e. accumulator registers 8(ps%2).. of key tile ps/2.
-template <int D, int BLK>
+template <int D, int BLK, bool FAST>
 struct Softmax {
   using F = Fa<D, BLK>;
   static constexpr int NE = F::QT * F::PS * 8;
@@ -329,7 +348,8 @@ struct Softmax {
   float p_even;  // probability of the last even element, packed with the next one
   __device__ __forceinline__ void element(int e) {
     const int i = e & 7, ps = (e >> 3) % F::PS, qt = (e >> 3) / F::PS;
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][qt][8 * (ps & 1) + i], scale_log2, -mb[qt]));
+    const float x = sacc[ps >> 1][qt][8 * (ps & 1) + i];
+    const float p = __builtin_amdgcn_exp2f(FAST ? x : __builtin_fmaf(x, scale_log2, -mb[qt]));
     if ((i & 1) == 0) {
       p_even = p;
     } else {
@@ -407,7 +427,7 @@ struct ListStream {
 //   softmax P(t) from S(t)                   (vector ALU, overlapping)
 //   PV      O += V(t)^T P(t) from V slot t%2
 //   wait for the copies, barrier.
-template <int D, int BLK>
+template <int D, int BLK, bool FAST>
 struct Pass {
   using F = Fa<D, BLK>;
   WaveState<D, BLK>& w;
@@ -446,7 +466,7 @@ struct Pass {
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) {
       w.l[qt] += lsum[qt];
-      w.bad |= lsum[qt] > kOverflowGuard;
+      w.bad |= lsum[qt] > (FAST ? kFastGuard : kOverflowGuard);
     }
   }
 
@@ -463,12 +483,12 @@ struct Pass {
   __device__ __forceinline__ void iter(f32x16 (&scur)[F::KTW][F::QT], f32x16 (&snext)[F::KTW][F::QT], int jv,
                                        int jk) {
     constexpr int NS = F::DS * F::KTW * F::QT;  // score MFMAs per block
-    constexpr int NE = Softmax<D, BLK>::NE;     // softmax elements per lane and block
+    constexpr int NE = Softmax<D, BLK, FAST>::NE;  // softmax elements per lane and block
     static_assert(NE % NS == 0 && (NE / NS) % 2 == 0, "softmax share per slot must be whole pairs");
     constexpr int EPS = NE / NS;
     constexpr int NC = 2 * F::SEGS;             // copies per wave and block
     bf16x8 pb[F::PS][F::QT];
-    Softmax<D, BLK> sm = {scur, pb, {}, scale_log2, 0.f};
+    Softmax<D, BLK, FAST> sm = {scur, pb, {}, scale_log2, 0.f};
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) sm.mb[qt] = w.m[qt] * scale_log2;
     const unsigned char* kb = sl.k[ST ^ 1];
@@ -515,13 +535,13 @@ struct Pass {
   // the V slot may be a runtime pointer).
   __device__ __forceinline__ void last(f32x16 (&scur)[F::KTW][F::QT], const unsigned char* vb) {
     bf16x8 pb[F::PS][F::QT];
-    Softmax<D, BLK> sm = {scur, pb, {}, scale_log2, 0.f};
+    Softmax<D, BLK, FAST> sm = {scur, pb, {}, scale_log2, 0.f};
 #pragma unroll
     for (int qt = 0; qt < F::QT; ++qt) sm.mb[qt] = w.m[qt] * scale_log2;
     bf16x8 vf[kVAhead + 1];
     pv_prefetch(vf, vb);
 #pragma unroll
-    for (int e = 0; e < Softmax<D, BLK>::NE; ++e) sm.element(e);
+    for (int e = 0; e < Softmax<D, BLK, FAST>::NE; ++e) sm.element(e);
     pv(pb, vb, vf);
     fence_agpr(w.oacc);  // O may be copied between registers after this point
     __syncthreads();
@@ -544,7 +564,18 @@ struct Pass {
     if (j1 >= 0) copy_tile<0, D, BLK>(cp, sl.k[1], j1);
     copy_tile<1, D, BLK>(cp, sl.v[0], j0);
     scores<D, BLK>(w, sl.k[0], sa);
-    if (first) tile_max<D, BLK>(sa, w.m);
+    if (first) {
+      tile_max<D, BLK>(sa, w.m);
+      if constexpr (FAST) {
+        // no reference maximum: the first block's maxima only decide whether
+        // the pass is safe
+#pragma unroll
+        for (int qt = 0; qt < F::QT; ++qt) {
+          w.bad |= !(__builtin_fabsf(w.m[qt]) <= kFastRange);
+          w.m[qt] = 0.f;
+        }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Steady state, two blocks per turn so that slots are compile-time
@@ -612,30 +643,51 @@ __device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* 
   return sg;
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_fa_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
-  using F = Fa<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_slot0[F::T];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_slot1[F::T];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_slot0[F::T];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_slot1[F::T];
-  const Slots sl = {{k_slot0, k_slot1}, {v_slot0, v_slot1}};
+// Arguments of one workgroup's row (or split segment): the kernel's, and
+// g, the workgroup's index after the XCD regrouping.
+struct RowArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* kv_idx;
+  const int32_t* kv_cnt;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int nq, nk, top_k, splits, g;
+  float scale_log2;
+};
 
+// One row (or split segment) of attention with the workgroup's LDS slots.
+// FAST: Q is multiplied by log2(e)/sqrt(d) once, in bf16, so a score is
+// already the exponent of its probability, and probabilities are exp2(s)
+// with no reference maximum subtracted (one VALU operation less per score).
+// That is the same softmax as long as nothing overflows or underflows; the
+// pass returns false without writing anything when a query's maximum over
+// the first listed block lies outside [-kFastRange, kFastRange] or a block's
+// probability sum reaches kFastGuard.  Otherwise (FAST = false): unscaled Q,
+// the first block's maximum as reference, and the rerun at the true maximum
+// described in the file header; always returns true.
+template <int D, int BLK, bool FAST>
+__device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
+  using F = Fa<D, BLK>;
+  const uint16_t* q = a.q;
+  const int32_t* kv_idx = a.kv_idx;
+  const int32_t* kv_cnt = a.kv_cnt;
+  const int nq = a.nq, nk = a.nk, top_k = a.top_k, splits = a.splits;
+  const float scale_log2 = a.scale_log2;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave % F::NQG, kg = wave / F::NQG;
   const int qc = lane & 31, hh = lane >> 5;
   const int kbase = kg * F::KW;
-  const Segment sg = segment_of(xcd_grouped(blockIdx.x, gridDim.x), splits, kv_cnt, top_k);
+  const Segment sg = segment_of(a.g, splits, kv_cnt, top_k);
   const int row = sg.row;
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
-  const uint16_t* kh = k + (size_t)bh * N * D;
-  const uint16_t* vh = v + (size_t)bh * N * D;
+  const uint16_t* kh = a.k + (size_t)bh * N * D;
+  const uint16_t* vh = a.v + (size_t)bh * N * D;
   ListStream ls;
   ls.list = kv_idx + (size_t)row * top_k + sg.begin;
   ls.cnt = sg.count;
@@ -651,7 +703,14 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
     for (int s = 0; s < F::DS; ++s) {
       const uint4 u = qrow[2 * s + hh];
-      __builtin_memcpy(&w.qf[qt][s], &u, 16);
+      if constexpr (FAST) {
+        bf16x8 raw;
+        __builtin_memcpy(&raw, &u, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w.qf[qt][s][e] = (__bf16)((float)raw[e] * scale_log2);
+      } else {
+        __builtin_memcpy(&w.qf[qt][s], &u, 16);
+      }
       asm volatile("" : "+a"(w.qf[qt][s]));  // Q lives in AGPRs
     }
     w.m[qt] = -__builtin_inff();
@@ -682,13 +741,13 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
   Copier<D, BLK> cp;
   cp.init(kh, vh, (uint32_t)(N * D * 2), wave, lane);
   w.bad = false;
-  Pass<D, BLK> pass = {w, sl, ls, cp, scale_log2, 0};
+  Pass<D, BLK, FAST> pass = {w, sl, ls, cp, scale_log2, 0};
   for (bool first = true;; first = false) {
     pass.run(lane, first);
     if (!first) break;
     // Did any lane of any wave see an overflow?  One flag per wave in a free
     // slot (every copy has landed and every wave has passed the last barrier).
-    int* flags = reinterpret_cast<int*>(v_slot0);
+    int* flags = reinterpret_cast<int*>(sl.v[0]);
     if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(w.bad) != 0;
     __syncthreads();
     int any_bad = 0;
@@ -696,6 +755,7 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
     for (int i = 0; i < F::NW; ++i) any_bad |= flags[i];
     __syncthreads();
     if (!any_bad) break;
+    if constexpr (FAST) return false;
     // Rare: some logit exceeded the first block's maximum by more than 40
     // log2-units.  Find each query's true maximum, then redo the row at it.
 #pragma unroll
@@ -718,11 +778,11 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
   // through LDS.  O of the kg = 1 waves fills both K slots exactly
   // (NQG * DT * QT * 16 registers of 64 lanes = 2 * BLK * D * 2 bytes).
   constexpr int HALF = F::NQG * F::DT * F::QT * 16 / 2;  // register slots per K slot
-  float* xm = reinterpret_cast<float*>(v_slot0);        // m: [qg][qt][lane], then l: [qg][qt][lane]
+  float* xm = reinterpret_cast<float*>(sl.v[0]);       // m: [qg][qt][lane], then l: [qg][qt][lane]
   auto xo_at = [&](int dt, int qt, int r) -> float* {
     const int f = ((qg * F::DT + dt) * F::QT + qt) * 16 + r;
-    return f < HALF ? reinterpret_cast<float*>(k_slot0) + f * 64 + lane
-                    : reinterpret_cast<float*>(k_slot1) + (f - HALF) * 64 + lane;
+    return f < HALF ? reinterpret_cast<float*>(sl.k[0]) + f * 64 + lane
+                    : reinterpret_cast<float*>(sl.k[1]) + (f - HALF) * 64 + lane;
   };
   float lw[F::QT];
 #pragma unroll
@@ -746,15 +806,16 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
       const float l1 = xm[((F::NQG + qg) * F::QT + qt) * 64 + lane];
       const float m0 = w.m[qt];
       const float mm = fmaxf(m0, m1);
-      const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * scale_log2);
-      const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * scale_log2);
+      const float msc = FAST ? 1.0f : scale_log2;  // reference maxima to log2 units
+      const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * msc);
+      const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * msc);
       const float lt = lw[qt] * a0 + l1 * a1;
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const size_t tq = qrow0 + 32 * qt + qc;
       // split mode: float32 partial result of this segment, token t of the block
       const size_t pt = ((size_t)sg.part * BLK + qg * F::QW + 32 * qt + qc);
-      uint16_t* orow = out + tq * D;
-      float* prow = part_o + pt * D;
+      uint16_t* orow = a.out + tq * D;
+      float* prow = a.part_o + pt * D;
 #pragma unroll
       for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
@@ -776,15 +837,40 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
         }
       }
       const float row_lse =
-          lt > 0.f ? (mm * scale_log2 + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+          lt > 0.f ? (mm * msc + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
       if (hh == 0) {
         if (splits)
-          part_lse[pt] = row_lse;
-        else if (lse)
-          lse[tq] = row_lse;
+          a.part_lse[pt] = row_lse;
+        else if (a.lse)
+          a.lse[tq] = row_lse;
       }
     }
   }
+  return true;
+}
+
+// The general pass, compiled as a function of its own so that its registers
+// do not constrain the fast pass inlined in the kernel.
+template <int D, int BLK>
+__device__ __attribute__((noinline)) void attend_row_general(const RowArgs a, const Slots sl) {
+  attend_row<D, BLK, false>(a, sl);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_fa_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int nq, int nk, int top_k, float scale_log2, int splits, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
+  using F = Fa<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_slot0[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_slot1[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_slot0[F::T];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_slot1[F::T];
+  const Slots sl = {{k_slot0, k_slot1}, {v_slot0, v_slot1}};
+  const RowArgs a = {q, k, v, kv_idx, kv_cnt, out, lse, part_o, part_lse, nq, nk, top_k, splits,
+                     xcd_grouped(blockIdx.x, gridDim.x), scale_log2};
+  if (!attend_row<D, BLK, true>(a, sl)) attend_row_general<D, BLK>(a, sl);
 }
 
 // float32 path: one thread per query token, K and V tiles staged in LDS.

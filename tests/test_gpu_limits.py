@@ -18,7 +18,8 @@ from oracle import velox_oracle as O
 from synth import make_inputs
 from synth.configs import Config
 from tests.gpu_helpers import dev_inputs, every_row_tokens, out_to_f64, say, to_dev
-from tests.parity_rules import BF16_MAX_ABS, BF16_MEAN_ABS, check_close, check_selection
+from tests.parity_rules import (BF16_MAX_ABS, BF16_MEAN_ABS, bf16_fast_lse_slack, check_close, check_lse,
+                                check_selection)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,5 +67,6 @@ def test_keep_all_with_8192_blocks():
     toks = np.array([0, 63, 64 * 17 + 5, cfg.chunk_tokens - 1], np.int64)
     ref, ref_lse = O.attn(x.q, x.k, x.v, full, cnt, cfg.block, tokens=toks)
     mx, mn = check_close(out_to_f64(out).reshape(-1, cfg.head_dim)[toks], ref, BF16_MAX_ABS, BF16_MEAN_ABS)
-    lmx, _ = check_close(lse.cpu().numpy().astype(np.float64).reshape(-1)[toks], ref_lse, 1e-3, 1e-3, "lse")
-    say(f"keep-all: max {mx:.3g} mean {mn:.3g}, lse max {lmx:.3g}")
+    slack = bf16_fast_lse_slack(x.q, x.k, full, cnt, cfg.block, toks)
+    lmx, smx = check_lse(lse.cpu().numpy().astype(np.float64).reshape(-1)[toks], ref_lse, slack)
+    say(f"keep-all: max {mx:.3g} mean {mn:.3g}, lse max excess over slack {lmx:.3g} (slack <= {smx:.3g})")

@@ -21,8 +21,8 @@ import geometry_routed_block_velox_amd as velox
 from oracle import velox_oracle as O
 from synth import get_config, make_inputs
 from tests.gpu_helpers import cached_inputs, dev_inputs, every_row_tokens, out_to_f64, say, to_dev
-from tests.parity_rules import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, check_close,
-                                check_selection)
+from tests.parity_rules import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, bf16_fast_lse_slack,
+                                check_close, check_lse, check_selection)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,8 +104,13 @@ def test_attention_matches_oracle_same_lists(name):
     say(f"{name}: oracle attention on {toks.size} tokens ({cfg.rows} rows)")
     ref, ref_lse = O.attn(x.q, x.k, x.v, r["kv_idx"], r["kv_cnt"], cfg.block, tokens=toks)
     mx, mn = check_close(out[toks], ref, *tol(cfg))
-    lmx, _ = check_close(lse[toks], ref_lse, 1e-3 if cfg.dtype == "bf16" else 1e-4, 1e-3, "lse")
-    say(f"{name}: out max {mx:.3g} mean {mn:.3g}; lse max {lmx:.3g}")
+    if cfg.dtype == "bf16":
+        slack = bf16_fast_lse_slack(x.q, x.k, r["kv_idx"], r["kv_cnt"], cfg.block, toks)
+        lmx, smx = check_lse(lse[toks], ref_lse, slack)
+        say(f"{name}: out max {mx:.3g} mean {mn:.3g}; lse max excess over slack {lmx:.3g} (slack <= {smx:.3g})")
+    else:
+        lmx, _ = check_close(lse[toks], ref_lse, 1e-4, 1e-3, "lse")
+        say(f"{name}: out max {mx:.3g} mean {mn:.3g}; lse max {lmx:.3g}")
 
 
 @pytest.mark.parametrize("name", ALL)

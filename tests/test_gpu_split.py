@@ -3,7 +3,9 @@
 Each row's list is cut into segments attended by separate workgroups and
 merged through their LSEs.  The merged result must meet the same bars as the
 unsplit kernel: max-abs 2e-2 / mean-abs 2e-3 (bf16) or 1e-4 / 1e-5 (float32)
-against the fp64 oracle on the same lists, LSE within 1e-3 (bf16) / 1e-4.
+against the fp64 oracle on the same lists; LSE within 1e-4 (float32), and for
+bf16 within 1e-3 plus the per-token slack of the fast pass's scaled Q (the
+LSE rule in parity_rules).
 Cases: split counts from 1 to more segments than listed blocks (empty
 segments), automatic split count, lists with invalid entries and empty rows.
 """
@@ -15,17 +17,14 @@ torch = pytest.importorskip("torch")
 import geometry_routed_block_velox_amd as velox
 from oracle import velox_oracle as O
 from tests.gpu_helpers import cached_inputs, dev_inputs, every_row_tokens, out_to_f64, say, to_dev
-from tests.parity_rules import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, check_close
+from tests.parity_rules import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, F32_MEAN_ABS, bf16_fast_lse_slack,
+                                check_close, check_lse)
 
 pytestmark = pytest.mark.gpu
 
 
 def tol(cfg):
     return (BF16_MAX_ABS, BF16_MEAN_ABS) if cfg.dtype == "bf16" else (F32_MAX_ABS, F32_MEAN_ABS)
-
-
-def lse_tol(cfg):
-    return 1e-3 if cfg.dtype == "bf16" else 1e-4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,8 +51,11 @@ def compare(x, kv_idx, kv_cnt, splits, toks=None, ref_idx=None, ref_cnt=None):
     ref_cnt = kv_cnt if ref_cnt is None else ref_cnt
     ref, ref_lse = O.attn(x.q, x.k, x.v, ref_idx, ref_cnt, cfg.block, tokens=toks)
     mx, mn = check_close(out[toks], ref, *tol(cfg))
-    lmx, _ = check_close(lse[toks], ref_lse, lse_tol(cfg), 1e-3, "lse")
-    say(f"{cfg.name}: splits={splits}: out max {mx:.3g} mean {mn:.3g}; lse max {lmx:.3g}")
+    if cfg.dtype == "bf16":
+        lmx, _ = check_lse(lse[toks], ref_lse, bf16_fast_lse_slack(x.q, x.k, kv_idx, kv_cnt, cfg.block, toks))
+    else:
+        lmx, _ = check_close(lse[toks], ref_lse, 1e-4, 1e-3, "lse")
+    say(f"{cfg.name}: splits={splits}: out max {mx:.3g} mean {mn:.3g}; lse max excess {lmx:.3g}")
     return out, lse
 
 

@@ -88,3 +88,41 @@ def test_bench_traffic_only_for_the_profiled_source(tmp_path):
     src = os.path.join(ROOT, "geometry_routed_block_velox_amd", "csrc", "sparse_fa.hip")
     expected = rec["hbm_bytes_per_launch"] if rec["kernel_source_sha"] == bench.file_sha(src) else None
     assert bench.traffic_from_profiles(src) == expected
+
+
+@pytest.mark.parametrize("kind", ["random", "constant-q", "large-logits"])
+def test_lse_slack_bounds_a_scaled_q_log_sum_exp(kind):
+    """The LSE slack of the parity rules is a bound: the log-sum-exp taken with
+    bf16(c q) in place of c q (exact fp64 arithmetic otherwise) stays within the
+    slack of the exact one, also when every q component rounds the same way."""
+    from synth.generate import bf16_bits_to_f32, f32_to_bf16_bits
+    from tests.parity_rules import bf16_fast_lse_slack
+    rng = np.random.default_rng(21)
+    B, H, T, d, blk, nk, k = 1, 2, 128, 64, 64, 6, 3
+    q = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    kk = rng.standard_normal((B, H, nk * blk, d)).astype(np.float32)
+    if kind == "constant-q":
+        q[:] = 1.0
+    if kind == "large-logits":
+        kk[:, :, 2 * blk:3 * blk] += 4.0
+    qb, kb = f32_to_bf16_bits(q), f32_to_bf16_bits(kk)
+    idx = np.stack([rng.permutation(nk)[:k] for _ in range(B * H * (T // blk))]).reshape(B, H, T // blk, k)
+    idx = idx.astype(np.int32)
+    cnt = np.full((B, H, T // blk), k, np.int32)
+    toks = np.arange(B * H * T)
+    slack = bf16_fast_lse_slack(qb, kb, idx, cnt, blk, toks)
+    qf = bf16_bits_to_f32(qb).reshape(-1, d).astype(np.float64)
+    c32 = np.float32(1.4426950408889634) / np.sqrt(np.float32(d))
+    qs = bf16_bits_to_f32(f32_to_bf16_bits(bf16_bits_to_f32(qb).reshape(-1, d) * c32)).astype(np.float64)
+    c = np.log2(np.e) / np.sqrt(d)
+    for t in toks:
+        bh, i = divmod(int(t) // blk, T // blk)
+        b, h = divmod(bh, H)
+        keys = (idx[b, h, i][:, None] * blk + np.arange(blk)).reshape(-1)
+        K = bf16_bits_to_f32(kb[b, h, keys]).astype(np.float64)
+        exact = K @ qf[t] * c
+        scaled = K @ qs[t]
+        lse_exact = np.log(2) * (exact.max() + np.log2(np.exp2(exact - exact.max()).sum()))
+        lse_scaled = np.log(2) * (scaled.max() + np.log2(np.exp2(scaled - scaled.max()).sum()))
+        assert abs(lse_scaled - lse_exact) <= slack[t] + 1e-9, (kind, t, lse_scaled - lse_exact, slack[t])
+    assert slack.max() > 0
