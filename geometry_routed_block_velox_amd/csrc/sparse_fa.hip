@@ -383,23 +383,36 @@ __device__ __forceinline__ void row_sums(const bf16x8 (&pb)[Fa<D, BLK>::PS][Fa<D
 struct ListStream {
   const int32_t* list;
   int cnt, nk;
+  int cap;        // entries that may be read; cnt <= cap, and cap does not depend on the loaded count
   int base;       // list position of the window's first entry
   int win, ahead; // this window's entries and the next window's (per lane)
   uint64_t mask;  // valid lanes of this window not handed out yet
+  static constexpr int PW = 4;  // windows loaded by prefetch (256 entries)
+  int raw[PW];    // those windows as loaded (entries at or past cnt not yet dropped)
 
   __device__ __forceinline__ int load(int b, int lane) const {
     return b + lane < cnt ? list[b + lane] : -1;
   }
-  __device__ __forceinline__ void start(int lane) {
-    base = 0;
-    win = load(0, lane);
-    ahead = load(64, lane);
-    mask = __builtin_amdgcn_ballot_w64((unsigned)win < (unsigned)nk);
+  // Issues the loads of the first PW windows: unconditional, straight-line
+  // and independent of cnt (positions past cap read entry cap - 1; start()
+  // drops everything at or past cnt <= cap), so that they go out together
+  // with the loads of the count and of Q and are waited for once, in start().
+  __device__ __forceinline__ void prefetch(int lane) {
+    const int last = cap > 0 ? cap - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) raw[i] = list[min(64 * i + lane, last)];
   }
-  // Number of valid entries in the whole list.
-  __device__ __forceinline__ int valid(int lane) const {
+  // Starts the stream at the first window (after prefetch); returns the
+  // number of valid entries in the whole list.
+  __device__ __forceinline__ int start(int lane) {
+    base = 0;
+    win = lane < cnt ? raw[0] : -1;
+    ahead = 64 + lane < cnt ? raw[1] : -1;
+    mask = __builtin_amdgcn_ballot_w64((unsigned)win < (unsigned)nk);
     int c = 0;
-    for (int t = lane; t < cnt; t += 64) c += (unsigned)list[t] < (unsigned)nk;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) c += (int)(64 * i + lane < cnt) & (int)((unsigned)raw[i] < (unsigned)nk);
+    for (int t = 64 * PW + lane; t < cnt; t += 64) c += (unsigned)list[t] < (unsigned)nk;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
     return __builtin_amdgcn_readfirstlane(c);
@@ -549,20 +562,35 @@ struct Pass {
 
   // One pass over the row's listed blocks.  With first the reference
   // maximum comes from the first listed block; otherwise w.m is given.
-  __device__ __forceinline__ void run(int lane, bool first) {
-    const int nvalid = ls.valid(lane);
-    if (nvalid == 0) return;
-    ls.start(lane);
+  // PREFETCHED: ls.prefetch has been called for this pass.  before_scores
+  // runs once, after the first copies are issued and before any score is
+  // computed (also for an empty list).
+  template <class BeforeScores>
+  __device__ __forceinline__ void run(int lane, bool first, bool prefetched, BeforeScores&& before_scores) {
+    if (!prefetched) ls.prefetch(lane);
+    const int nvalid = ls.start(lane);
+    if (nvalid == 0) {
+      before_scores();
+      return;
+    }
     const int j0 = ls.take(lane);
     int j1 = ls.take(lane), j2 = ls.take(lane);
     fallback = j0;
+    // block ids of t+1 and t+2, taken an iteration ahead; past the end of
+    // the list (the phantom step, the K copy for a block that does not
+    // exist) the fallback is copied and never used
+    if (j1 < 0) j1 = fallback;
+    if (j2 < 0) j2 = fallback;
     f32x16 sa[F::KTW][F::QT], sb[F::KTW][F::QT];
-    // block 0: K into slot 0; then its scores while K(1) and V(0) are copied
+    // block 0: K(0), K(1) and V(0) are copied together.  The scores of block 0
+    // wait only for K(0): this wave's copies of it are the oldest, so
+    // vmcnt(2 * SEGS) leaves K(1) and V(0) in flight, and the barrier covers
+    // the other waves' copies.
     copy_tile<0, D, BLK>(cp, sl.k[0], j0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j1 >= 0) copy_tile<0, D, BLK>(cp, sl.k[1], j1);
+    copy_tile<0, D, BLK>(cp, sl.k[1], j1);
     copy_tile<1, D, BLK>(cp, sl.v[0], j0);
+    before_scores();
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * F::SEGS) : "memory");
     scores<D, BLK>(w, sl.k[0], sa);
     if (first) {
       tile_max<D, BLK>(sa, w.m);
@@ -585,11 +613,6 @@ struct Pass {
     // last block always sits in slot 0 and there is a single loop exit.
     const int steps = nvalid - 1;
     const bool phantom = steps & 1;
-    // block ids of t+1 and t+2, taken an iteration ahead; past the end of
-    // the list (the phantom step, the K copy for a block that does not
-    // exist) the fallback is copied and never used
-    if (j1 < 0) j1 = fallback;
-    if (j2 < 0) j2 = fallback;
     for (int turn = 0; turn < (steps + 1) / 2; ++turn) {
       int j3 = ls.take(lane);
       iter<0>(sa, sb, j1, j2);
@@ -607,6 +630,7 @@ struct Pass {
   // Rare path: the true maximum of every query over the listed blocks (no softmax, no V).
   __device__ __forceinline__ void max_sweep(int lane) {
     f32x16 sa[F::KTW][F::QT];
+    ls.prefetch(lane);
     ls.start(lane);
     for (int j = ls.take(lane); j >= 0; j = ls.take(lane)) {
       copy_tile<0, D, BLK>(cp, sl.k[0], j);
@@ -631,15 +655,23 @@ struct Segment {
   int row, begin, count, part;
 };
 
+// SPLIT = false: the whole row, at list position 0 (known before the count
+// is loaded).
+template <bool SPLIT>
 __device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* __restrict__ kv_cnt, int top_k) {
   Segment sg;
-  const int parts = splits > 0 ? splits : 1;
-  sg.row = g / parts;
+  const int parts = SPLIT ? splits : 1;
+  sg.row = SPLIT ? g / parts : g;
   sg.part = g;
   const int cnt = min(max(kv_cnt[sg.row], 0), top_k);
-  const int s = g % parts;
-  sg.begin = (int)(((long long)s * cnt) / parts);
-  sg.count = (int)(((long long)(s + 1) * cnt) / parts) - sg.begin;
+  if constexpr (SPLIT) {
+    const int s = g % parts;
+    sg.begin = (int)(((long long)s * cnt) / parts);
+    sg.count = (int)(((long long)(s + 1) * cnt) / parts) - sg.begin;
+  } else {
+    sg.begin = 0;
+    sg.count = cnt;
+  }
   return sg;
 }
 
@@ -669,7 +701,7 @@ struct RowArgs {
 // probability sum reaches kFastGuard.  Otherwise (FAST = false): unscaled Q,
 // the first block's maximum as reference, and the rerun at the true maximum
 // described in the file header; always returns true.
-template <int D, int BLK, bool FAST>
+template <int D, int BLK, bool FAST, bool SPLIT>
 __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   using F = Fa<D, BLK>;
   const uint16_t* q = a.q;
@@ -682,7 +714,17 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   const int qg = wave % F::NQG, kg = wave / F::NQG;
   const int qc = lane & 31, hh = lane >> 5;
   const int kbase = kg * F::KW;
-  const Segment sg = segment_of(a.g, splits, kv_cnt, top_k);
+  // The row's loads go out together: its count, its list, then its Q.  Each
+  // is waited for where it is used, the count only after Q has been issued.
+  Segment sg;
+  int cnt_raw = 0;
+  if constexpr (SPLIT) {
+    sg = segment_of<true>(a.g, splits, kv_cnt, top_k);
+  } else {
+    sg.row = sg.part = a.g;
+    sg.begin = 0;
+    cnt_raw = kv_cnt[sg.row];
+  }
   const int row = sg.row;
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
@@ -690,29 +732,48 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   const uint16_t* vh = a.v + (size_t)bh * N * D;
   ListStream ls;
   ls.list = kv_idx + (size_t)row * top_k + sg.begin;
-  ls.cnt = sg.count;
   ls.nk = nk;
+  ls.cap = SPLIT ? sg.count : top_k;
+  ls.prefetch(lane);
+  asm volatile("" ::: "memory");  // the list stays ahead of Q: the copies wait for it, not for Q
 
   WaveState<D, BLK> w;
   const size_t qrow0 = (size_t)bh * nq * BLK + (size_t)iq * BLK + qg * F::QW;
+  // The row's Q is loaded now, right behind its list, and moved into the
+  // B-operand fragments (take_q) only where the pass needs it, so that the
+  // latencies of the list, Q and the first copies overlap.
+  uint4 qraw[F::QT][F::DS];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) {
     // B operand of S^T = K Q^T: lane l holds query 32qt + l%32 of this wave's
     // group, d = 16s + 8(l/32) + 0..7
     const uint4* qrow = reinterpret_cast<const uint4*>(q + (qrow0 + 32 * qt + qc) * D);
 #pragma unroll
-    for (int s = 0; s < F::DS; ++s) {
-      const uint4 u = qrow[2 * s + hh];
-      if constexpr (FAST) {
-        bf16x8 raw;
-        __builtin_memcpy(&raw, &u, 16);
+    for (int s = 0; s < F::DS; ++s) qraw[qt][s] = qrow[2 * s + hh];
+  }
+  if constexpr (!SPLIT) {
+    asm volatile("" : "+v"(cnt_raw));  // not used before this point
+    sg.count = __builtin_amdgcn_readfirstlane(min(max(cnt_raw, 0), top_k));
+  }
+  ls.cnt = sg.count;
+  auto take_q = [&]() {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w.qf[qt][s][e] = (__bf16)((float)raw[e] * scale_log2);
-      } else {
-        __builtin_memcpy(&w.qf[qt][s], &u, 16);
+    for (int qt = 0; qt < F::QT; ++qt)
+#pragma unroll
+      for (int s = 0; s < F::DS; ++s) {
+        if constexpr (FAST) {
+          bf16x8 raw;
+          __builtin_memcpy(&raw, &qraw[qt][s], 16);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w.qf[qt][s][e] = (__bf16)((float)raw[e] * scale_log2);
+        } else {
+          __builtin_memcpy(&w.qf[qt][s], &qraw[qt][s], 16);
+        }
+        asm volatile("" : "+a"(w.qf[qt][s]));  // Q lives in AGPRs
       }
-      asm volatile("" : "+a"(w.qf[qt][s]));  // Q lives in AGPRs
-    }
+  };
+#pragma unroll
+  for (int qt = 0; qt < F::QT; ++qt) {
     w.m[qt] = -__builtin_inff();
     w.l[qt] = 0.f;
 #pragma unroll
@@ -743,7 +804,18 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   w.bad = false;
   Pass<D, BLK, FAST> pass = {w, sl, ls, cp, scale_log2, 0};
   for (bool first = true;; first = false) {
-    pass.run(lane, first);
+    // Q is taken before the fast pass (it arrives together with the list the
+    // pass waits for first) and, in the general pass, after its first copies;
+    // these placements keep the block loop's code as tight as before and the
+    // general pass free of AGPR rewrites next to its MFMAs.
+    if (!first) {
+      pass.run(lane, false, false, [] {});
+    } else if constexpr (FAST) {
+      take_q();
+      pass.run(lane, true, true, [] {});
+    } else {
+      pass.run(lane, true, true, take_q);
+    }
     if (!first) break;
     // Did any lane of any wave see an overflow?  One flag per wave in a free
     // slot (every copy has landed and every wave has passed the last barrier).
@@ -779,10 +851,11 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   // (NQG * DT * QT * 16 registers of 64 lanes = 2 * BLK * D * 2 bytes).
   constexpr int HALF = F::NQG * F::DT * F::QT * 16 / 2;  // register slots per K slot
   float* xm = reinterpret_cast<float*>(sl.v[0]);       // m: [qg][qt][lane], then l: [qg][qt][lane]
-  auto xo_at = [&](int dt, int qt, int r) -> float* {
-    const int f = ((qg * F::DT + dt) * F::QT + qt) * 16 + r;
-    return f < HALF ? reinterpret_cast<float*>(sl.k[0]) + f * 64 + lane
-                    : reinterpret_cast<float*>(sl.k[1]) + (f - HALF) * 64 + lane;
+  // registers 4rq..4rq+3 of accumulator (dt, qt): one 16-byte LDS access per lane
+  auto xo_at = [&](int dt, int qt, int rq) -> float4* {
+    const int f = ((qg * F::DT + dt) * F::QT + qt) * 4 + rq;
+    return f < HALF / 4 ? reinterpret_cast<float4*>(sl.k[0]) + f * 64 + lane
+                        : reinterpret_cast<float4*>(sl.k[1]) + (f - HALF / 4) * 64 + lane;
   };
   float lw[F::QT];
 #pragma unroll
@@ -795,7 +868,9 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
 #pragma unroll
       for (int dt = 0; dt < F::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) *xo_at(dt, qt, r) = w.oacc[dt][qt][r];
+        for (int rq = 0; rq < 4; ++rq)
+          *xo_at(dt, qt, rq) = make_float4(w.oacc[dt][qt][4 * rq], w.oacc[dt][qt][4 * rq + 1],
+                                           w.oacc[dt][qt][4 * rq + 2], w.oacc[dt][qt][4 * rq + 3]);
     }
   }
   __syncthreads();
@@ -820,13 +895,12 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
       for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
+          const float4 x = *xo_at(dt, qt, rq);
+          const float xe[4] = {x.x, x.y, x.z, x.w};
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            o[e] = (w.oacc[dt][qt][r] * a0 + *xo_at(dt, qt, r) * a1) * inv;
-          }
-          if (splits) {
+          for (int e = 0; e < 4; ++e) o[e] = (w.oacc[dt][qt][4 * rq + e] * a0 + xe[e] * a1) * inv;
+          if constexpr (SPLIT) {
             *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * hh) = make_float4(o[0], o[1], o[2], o[3]);
           } else {
             uint2 pk;
@@ -839,7 +913,7 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
       const float row_lse =
           lt > 0.f ? (mm * msc + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
       if (hh == 0) {
-        if (splits)
+        if constexpr (SPLIT)
           a.part_lse[pt] = row_lse;
         else if (a.lse)
           a.lse[tq] = row_lse;
@@ -851,12 +925,13 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
 
 // The general pass, compiled as a function of its own so that its registers
 // do not constrain the fast pass inlined in the kernel.
-template <int D, int BLK>
+template <int D, int BLK, bool SPLIT>
 __device__ __attribute__((noinline)) void attend_row_general(const RowArgs a, const Slots sl) {
-  attend_row<D, BLK, false>(a, sl);
+  attend_row<D, BLK, false, SPLIT>(a, sl);
 }
 
-template <int D, int BLK>
+// SPLIT: split-KV segments (splits > 0) instead of whole rows.
+template <int D, int BLK, bool SPLIT>
 __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_fa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ out,
@@ -870,7 +945,7 @@ __global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const Slots sl = {{k_slot0, k_slot1}, {v_slot0, v_slot1}};
   const RowArgs a = {q, k, v, kv_idx, kv_cnt, out, lse, part_o, part_lse, nq, nk, top_k, splits,
                      xcd_grouped(blockIdx.x, gridDim.x), scale_log2};
-  if (!attend_row<D, BLK, true>(a, sl)) attend_row_general<D, BLK>(a, sl);
+  if (!attend_row<D, BLK, true, SPLIT>(a, sl)) attend_row_general<D, BLK, SPLIT>(a, sl);
 }
 
 // float32 path: one thread per query token, K and V tiles staged in LDS.
@@ -888,7 +963,8 @@ __global__ __launch_bounds__(BLK) void sparse_fa_f32_kernel(const float* __restr
   float* kt = fs;
   float* vt = fs + BLK * D;
   const int tid = threadIdx.x;
-  const Segment sg = segment_of(blockIdx.x, splits, kv_cnt, top_k);
+  const Segment sg = splits > 0 ? segment_of<true>(blockIdx.x, splits, kv_cnt, top_k)
+                                 : segment_of<false>(blockIdx.x, splits, kv_cnt, top_k);
   const int row = sg.row;
   const int bh = row / nq, iq = row % nq;
   const size_t N = (size_t)nk * BLK;
@@ -1001,8 +1077,9 @@ hipError_t fa_bf16(const Dims& x, const void* q, const void* k, const void* v, c
                    hipStream_t s) {
   const int rows = x.B * x.H * x.nq;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((sparse_fa_bf16_kernel<D, BLK>), dim3(rows * (splits > 0 ? splits : 1)), dim3(Fa<D, BLK>::NT),
-                     0, s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  auto kern = splits > 0 ? sparse_fa_bf16_kernel<D, BLK, true> : sparse_fa_bf16_kernel<D, BLK, false>;
+  hipLaunchKernelGGL(kern, dim3(rows * (splits > 0 ? splits : 1)), dim3(Fa<D, BLK>::NT), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), kv_idx, kv_cnt, static_cast<uint16_t*>(out), lse, x.nq, x.nk,
                      x.top_k, scale_log2, splits, part_o, part_lse);
   return hipGetLastError();
