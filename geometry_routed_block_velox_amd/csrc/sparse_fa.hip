@@ -675,6 +675,13 @@ __device__ __forceinline__ Segment segment_of(int g, int splits, const int32_t* 
   return sg;
 }
 
+// A query tile index as a type, so that code taking it indexes accumulator
+// registers with a compile-time constant.
+template <int I>
+struct QTile {
+  static constexpr int value = I;
+};
+
 // Arguments of one workgroup's row (or split segment): the kernel's, and
 // g, the workgroup's index after the XCD regrouping.
 struct RowArgs {
@@ -846,9 +853,12 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   __syncthreads();
   fence_agpr(w.oacc);  // the last PV MFMAs have written O before it is read
 
-  // Merge the two key halves: waves with kg = 1 hand (m, l, O) to kg = 0
-  // through LDS.  O of the kg = 1 waves fills both K slots exactly
-  // (NQG * DT * QT * 16 registers of 64 lanes = 2 * BLK * D * 2 bytes).
+  // Merge the two key halves.  The two waves of a query group split the work
+  // by query tile: wave kg hands (m, l, O) of query tile 1 - kg to its
+  // partner through LDS and merges query tile kg.  The handed-over O fills
+  // both K slots exactly (2 * NQG waves * DT * 16 registers of 64 lanes =
+  // 2 * BLK * D * 2 bytes).
+  static_assert(F::QT == 2, "one query tile per key half");
   constexpr int HALF = F::NQG * F::DT * F::QT * 16 / 2;  // register slots per K slot
   float* xm = reinterpret_cast<float*>(sl.v[0]);       // m: [qg][qt][lane], then l: [qg][qt][lane]
   // registers 4rq..4rq+3 of accumulator (dt, qt): one 16-byte LDS access per lane
@@ -860,66 +870,70 @@ __device__ __forceinline__ bool attend_row(const RowArgs a, const Slots sl) {
   float lw[F::QT];
 #pragma unroll
   for (int qt = 0; qt < F::QT; ++qt) lw[qt] = w.l[qt] + __shfl_xor(w.l[qt], 32);
-  if (kg == 1) {
+  auto hand_over = [&](auto tile) {
+    constexpr int qt = decltype(tile)::value;
+    xm[(qg * F::QT + qt) * 64 + lane] = w.m[qt];
+    xm[((F::NQG + qg) * F::QT + qt) * 64 + lane] = lw[qt];
 #pragma unroll
-    for (int qt = 0; qt < F::QT; ++qt) {
-      xm[(qg * F::QT + qt) * 64 + lane] = w.m[qt];
-      xm[((F::NQG + qg) * F::QT + qt) * 64 + lane] = lw[qt];
+    for (int dt = 0; dt < F::DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < F::DT; ++dt)
+      for (int rq = 0; rq < 4; ++rq)
+        *xo_at(dt, qt, rq) = make_float4(w.oacc[dt][qt][4 * rq], w.oacc[dt][qt][4 * rq + 1],
+                                         w.oacc[dt][qt][4 * rq + 2], w.oacc[dt][qt][4 * rq + 3]);
+  };
+  auto merge = [&](auto tile) {
+    constexpr int qt = decltype(tile)::value;
+    const float m1 = xm[(qg * F::QT + qt) * 64 + lane];
+    const float l1 = xm[((F::NQG + qg) * F::QT + qt) * 64 + lane];
+    const float m0 = w.m[qt];
+    const float mm = fmaxf(m0, m1);
+    const float msc = FAST ? 1.0f : scale_log2;  // reference maxima to log2 units
+    const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * msc);
+    const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * msc);
+    const float lt = lw[qt] * a0 + l1 * a1;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const size_t tq = qrow0 + 32 * qt + qc;
+    // split mode: float32 partial result of this segment, token t of the block
+    const size_t pt = ((size_t)sg.part * BLK + qg * F::QW + 32 * qt + qc);
+    uint16_t* orow = a.out + tq * D;
+    float* prow = a.part_o + pt * D;
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *xo_at(dt, qt, rq) = make_float4(w.oacc[dt][qt][4 * rq], w.oacc[dt][qt][4 * rq + 1],
-                                           w.oacc[dt][qt][4 * rq + 2], w.oacc[dt][qt][4 * rq + 3]);
-    }
-  }
-  __syncthreads();
-  if (kg == 0) {
+    for (int dt = 0; dt < F::DT; ++dt) {
 #pragma unroll
-    for (int qt = 0; qt < F::QT; ++qt) {
-      const float m1 = xm[(qg * F::QT + qt) * 64 + lane];
-      const float l1 = xm[((F::NQG + qg) * F::QT + qt) * 64 + lane];
-      const float m0 = w.m[qt];
-      const float mm = fmaxf(m0, m1);
-      const float msc = FAST ? 1.0f : scale_log2;  // reference maxima to log2 units
-      const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * msc);
-      const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * msc);
-      const float lt = lw[qt] * a0 + l1 * a1;
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      const size_t tq = qrow0 + 32 * qt + qc;
-      // split mode: float32 partial result of this segment, token t of the block
-      const size_t pt = ((size_t)sg.part * BLK + qg * F::QW + 32 * qt + qc);
-      uint16_t* orow = a.out + tq * D;
-      float* prow = a.part_o + pt * D;
+      for (int rq = 0; rq < 4; ++rq) {
+        const float4 x = *xo_at(dt, qt, rq);
+        const float xe[4] = {x.x, x.y, x.z, x.w};
+        float o[4];
 #pragma unroll
-      for (int dt = 0; dt < F::DT; ++dt) {
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const float4 x = *xo_at(dt, qt, rq);
-          const float xe[4] = {x.x, x.y, x.z, x.w};
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (w.oacc[dt][qt][4 * rq + e] * a0 + xe[e] * a1) * inv;
-          if constexpr (SPLIT) {
-            *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * hh) = make_float4(o[0], o[1], o[2], o[3]);
-          } else {
-            uint2 pk;
-            pk.x = pack_bf16x2(o[0], o[1]);
-            pk.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * hh) = pk;
-          }
+        for (int e = 0; e < 4; ++e) o[e] = (w.oacc[dt][qt][4 * rq + e] * a0 + xe[e] * a1) * inv;
+        if constexpr (SPLIT) {
+          *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * hh) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint2 pk;
+          pk.x = pack_bf16x2(o[0], o[1]);
+          pk.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * hh) = pk;
         }
       }
-      const float row_lse =
-          lt > 0.f ? (mm * msc + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
-      if (hh == 0) {
-        if constexpr (SPLIT)
-          a.part_lse[pt] = row_lse;
-        else if (a.lse)
-          a.lse[tq] = row_lse;
-      }
     }
-  }
+    const float row_lse =
+        lt > 0.f ? (mm * msc + __builtin_log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+    if (hh == 0) {
+      if constexpr (SPLIT)
+        a.part_lse[pt] = row_lse;
+      else if (a.lse)
+        a.lse[tq] = row_lse;
+    }
+  };
+  if (kg == 0)
+    hand_over(QTile<1>{});
+  else
+    hand_over(QTile<0>{});
+  __syncthreads();
+  if (kg == 0)
+    merge(QTile<0>{});
+  else
+    merge(QTile<1>{});
   return true;
 }
 
