@@ -194,14 +194,22 @@ def test_unsorted_and_repeated_lists():
 
 
 @pytest.mark.parametrize("case", ["dominant-block", "two-close-blocks", "float32-overflow"])
-@pytest.mark.parametrize("base,extra", [("small", False), ("mid", False), ("mid", True)])
+@pytest.mark.parametrize("base,extra", [("small", False), ("mid", False), ("mid", True), ("d128-blk64", False),
+                                        ("d64-blk128", True)])
 def test_logits_far_above_first_block_recompute_row(case, base, extra):
-    """Logits more than 40 log2-units above the first listed block's maximum make
-    the kernel redo the row at the true maximum; the result must still match.
-    d = 64 / blk = 64 and d = 128 / blk = 128 kernels, lists of 4 and 5 blocks
-    (both exits of the two-blocks-per-turn loop)."""
+    """Large logits take every path of the kernel and must still match:
+    two-close-blocks stays in the fast pass (base-2 logits of about 46);
+    dominant-block and float32-overflow leave it (probability sums past 2^56)
+    for the general pass, whose first block is then more than 40 log2-units
+    below the maximum, so it reruns the row at the true maximum.  All four
+    (d, blk) kernels, lists of 4 and 5 blocks (both exits of the
+    two-blocks-per-turn loop)."""
     if base == "small":
         cfg = get_config("small").with_(heads=2, chunk_tokens=128, past_chunks=4)
+    elif base == "d128-blk64":
+        cfg = get_config("mid").with_(heads=2, chunk_tokens=256, past_chunks=4, block=64)
+    elif base == "d64-blk128":
+        cfg = get_config("small").with_(heads=2, chunk_tokens=256, past_chunks=4, block=128)
     else:
         cfg = get_config("mid").with_(heads=2, chunk_tokens=256, past_chunks=4)
     x = make_inputs(cfg)
