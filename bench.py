@@ -37,6 +37,25 @@ def parse():
     return ap.parse_args()
 
 
+def timed_ahead(fn, reps, stream):
+    """GPU time per call of `fn` run back to back: the stream first runs a spin kernel
+    long enough for the host to enqueue all `reps` calls behind it, so the figure is
+    the calls' device time, not the host's launch rate (these calls take tens of us)."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(400_000 * reps)  # >= ~150 us of host time per call at <= 2.4 GHz
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def file_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -262,16 +281,7 @@ def bench_overlap_builder(velox, cfg, x, q, k, ws, stream, reps=20):
         velox.select(s, ov, cov, cfg.block, cfg.top_k, cfg.alpha, stream=stream)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return timed_ahead(fn, reps, stream)
 
     t_builder = timed(lambda: velox.frustum_overlap(yaw, pd, qd, fov, out=(ov, cov), stream=stream))
     t_seq, t_conc = timed(sequential), timed(concurrent)
@@ -300,15 +310,8 @@ def bench_split_small(velox, stream, reps=50):
     f_exec = 4.0 * cfg.head_dim * cfg.block * cfg.block * float(kv_cnt.sum())
 
     def timed(splits):
-        for _ in range(3):
-            velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out, splits=splits, workspace=ws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out, splits=splits, workspace=ws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return timed_ahead(lambda: velox.sparse_attn(q, k, v, kv_idx, kv_cnt, cfg.block, out=out, splits=splits,
+                                                     workspace=ws), reps, stream)
 
     t1, ts = timed(None), timed(n)
     return {"workload": f"small: B1 H4 d64 T1024 chunk12 blk64 top-k48 ({cfg.rows} rows)", "splits": n,
@@ -329,13 +332,7 @@ def bench_route_log_prob(velox, cfg, q, k, ov, cov, kv_idx, ws, stream, reps=20)
     call()
     torch.cuda.synchronize()
     changed = int((idx2 != kv_idx).any(dim=-1).sum())
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return {"ms": round(e0.elapsed_time(e1) / reps, 4), "rows_with_different_list": changed,
+    return {"ms": round(timed_ahead(call, reps, stream), 4), "rows_with_different_list": changed,
             "rows": cfg.rows}
 
 
@@ -354,27 +351,18 @@ def bench_route_cached(velox, cfg, q, k, ov, cov, kv_idx, kv_cnt, ws, stream, el
     call()
     torch.cuda.synchronize()
     same = bool(torch.equal(idx2, kv_idx) and torch.equal(cnt2, kv_cnt))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = timed_ahead(call, reps, stream)
     nbytes = q.numel() * el + B * H * past * d * 4 + small_bytes
     gbs = nbytes / (ms * 1e-3) / 1e9
     # one-time cost per finished chunk: pooling its nq blocks into the cache
-    e0.record(stream)
-    for _ in range(reps):
-        velox.pool_keys(k, cfg.chunk_tokens, cfg.block, max(past - nq, 0), min(nq, past), kbar=kbar)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    pool_ms = e0.elapsed_time(e1) / reps
+    pool_ms = timed_ahead(lambda: velox.pool_keys(k, cfg.chunk_tokens, cfg.block, max(past - nq, 0), min(nq, past),
+                                                  kbar=kbar), reps, stream)
     return {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "identical_to_route": same,
             "pool_one_chunk_ms": round(pool_ms, 4),
             "note": "velox_route_cached with the past chunks' pooled keys cached; pool_one_chunk_ms is the "
-                    "once-per-chunk velox_pool_keys cost of appending a finished chunk"}
+                    "once-per-chunk velox_pool_keys cost of appending a finished chunk; device time of "
+                    "back-to-back calls (the host enqueues them behind a spin kernel)"}
 
 
 def cpu_model_name():
