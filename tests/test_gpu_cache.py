@@ -119,3 +119,37 @@ def test_cache_rejects_short_cache():
         velox.route_cached(d["q"], kbar, cfg.past_chunks, d["overlap"], d["covered"], cfg.block, cfg.top_k, cfg.alpha)
     with pytest.raises(velox.VeloxError):
         velox.pool_keys(d["k"], cfg.chunk_tokens, cfg.block, cfg.nk - 2, 3)
+
+
+# query-block counts that leave the scoring's 16-row tiles partly empty (24 -> two
+# tiles, 40 -> four), for both head sizes
+ODD_TILES = [
+    ("nq24-d64-b64", "small", dict(heads=2, chunk_tokens=1536, past_chunks=3, block=64, top_k=36)),
+    ("nq40-d128-b128", "mid", dict(heads=1, chunk_tokens=5120, past_chunks=2, block=128, top_k=56)),
+]
+
+
+@pytest.mark.parametrize("label,base,kw", ODD_TILES, ids=[t[0] for t in ODD_TILES])
+def test_partial_query_tiles(label, base, kw):
+    """velox_route against the oracle's gap rule, and velox_route_cached bit-identical to it
+    (lists and returned scores), where the last query tile is only partly filled."""
+    from synth import get_config, make_inputs
+    cfg = get_config(base).with_(name=label, **kw)
+    assert cfg.nq % 16 != 0
+    x = make_inputs(cfg)
+    d = dev_inputs(x)
+    say(f"{label}: nq {cfg.nq} nk {cfg.nk}: velox_route")
+    ref_idx, ref_cnt, ref_s = velox.route(d["q"], d["k"], d["overlap"], d["covered"], cfg.block, cfg.top_k,
+                                          cfg.alpha, return_scores=True)
+    torch.cuda.synchronize()
+    r = O.route(x.q, x.k, x.overlap, x.covered, cfg.block, cfg.top_k, cfg.alpha)
+    st = check_selection(ref_idx.cpu().numpy(), ref_cnt.cpu().numpy(), r["m"], r["kth"], r["kv_idx"], cfg.k_eff,
+                         cfg.nk - cfg.ncur)
+    say(f"{label}: selection {st}")
+    say(f"{label}: velox_route_cached with scores")
+    kbar = fill_cache_by_chunk(d["k"], cfg, spare_chunks=1, upto_chunk=cfg.past_chunks + 1)
+    idx, cnt, s = velox.route_cached(d["q"], kbar, cfg.past_chunks, d["overlap"], d["covered"], cfg.block,
+                                     cfg.top_k, cfg.alpha, return_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref_idx) and torch.equal(cnt, ref_cnt)
+    assert torch.equal(s.view(torch.int32), ref_s.view(torch.int32)), "scores differ bitwise"
