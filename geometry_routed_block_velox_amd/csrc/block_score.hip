@@ -55,19 +55,21 @@ struct F32In {
   }
 };
 
-// One wave sums ROWS rows of D elements at `src`; on return lanes 0..CPR-1
-// hold the sums of columns [VEC*lane, VEC*lane + VEC) in acc.  Lane l reads
-// 16-byte chunk l % CPR of rows l / CPR + RPI * it, so every wave-wide load
-// is one contiguous 1 KiB span of the rows.
-template <class E, int D, int ROWS>
-__device__ __forceinline__ void wave_sum(const typename E::T* __restrict__ src, float (&acc)[E::VEC], int lane) {
+// One wave pools a [BLK, D] block at `src` into D floats at `dst`
+// (written by the first CPR lanes).  Lane l reads 16-byte chunk l % CPR of
+// rows l / CPR + RPI * it, so every wave-wide load is one contiguous 1 KiB
+// span of the block.
+template <class E, int D, int BLK>
+__device__ __forceinline__ void wave_pool(const typename E::T* __restrict__ src, float* __restrict__ dst,
+                                          int lane) {
   constexpr int VEC = E::VEC;
   constexpr int CPR = D / VEC;   // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;  // rows per wave-wide load
-  constexpr int NIT = ROWS / RPI;
-  static_assert(CPR <= 64 && 64 % CPR == 0 && ROWS % RPI == 0, "bad pooling shape");
+  constexpr int NIT = BLK / RPI;
+  static_assert(CPR <= 64 && 64 % CPR == 0 && BLK % RPI == 0, "bad pooling shape");
   const int c = lane % CPR;
   const u32x4* p = reinterpret_cast<const u32x4*>(src) + (lane / CPR) * CPR + c;
+  float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
   // Loads are issued in batches of up to 16 (64 VGPRs) before they are consumed.
@@ -85,18 +87,9 @@ __device__ __forceinline__ void wave_sum(const typename E::T* __restrict__ src, 
   for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
-}
-
-// One wave pools a [BLK, D] block at `src` into D floats at `dst`.
-template <class E, int D, int BLK>
-__device__ __forceinline__ void wave_pool(const typename E::T* __restrict__ src, float* __restrict__ dst,
-                                          int lane) {
-  constexpr int VEC = E::VEC, CPR = D / VEC;
-  float acc[VEC];
-  wave_sum<E, D, BLK>(src, acc, lane);
   if (lane < CPR) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) dst[lane * VEC + v] = acc[v] * (1.0f / BLK);
+    for (int v = 0; v < VEC; ++v) dst[c * VEC + v] = acc[v] * (1.0f / BLK);
   }
 }
 
