@@ -123,7 +123,8 @@ size_t velox_route_workspace_bytes(const velox_problem *p);
  *                                     velox_route_workspace_bytes(p) bytes, 256-byte aligned
  *
  * Per row (b,h,i): qbar_i and kbar_j are the means of Q over query block i
- * and of K over KV block j (float32 sums); s_j = <qbar_i, kbar_j>/sqrt(d);
+ * and of K over KV block j (float32 sums); s_j = <qbar_i, kbar_j>/sqrt(d)
+ * (float32 matrix-core products and sums);
  * m_j = +inf for current-chunk blocks, the modulated importance of
  * p->modulation with o = overlap[b,i,chunk(j)] for past blocks of covered
  * rows (s_j*(1 + alpha*o) by default), s_j otherwise (every operation a
