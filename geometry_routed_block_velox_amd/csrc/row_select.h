@@ -85,11 +85,12 @@ constexpr int kMaxKpt = 32;
 // byte (most of a row) mostly hit different banks instead of one address.
 constexpr int kSelCopies = 8;
 
-// LDS of one row selection.
+// LDS of one row selection (the per-wave counts are an int4: four waves).
+static_assert(kSelThreads == 256, "one int4 of per-wave counts");
 struct SelectShared {
   uint32_t part[kSelCopies][257];  // first pass: per-copy counts
   uint32_t hist[3][256];           // first-pass totals, then the histograms of passes 2-4 (rotating)
-  int4 wave_cnt[2][kMaxKpt];       // per key round: above-K* / equal-to-K* counts of the 4 waves
+  int4 wave_cnt[2][kMaxKpt];       // per key round: above / matching the final prefix, per wave
 };
 
 // Digit of the rank-kr key among the counts h[0..255] (ranked from digit 255
