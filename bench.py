@@ -46,8 +46,10 @@ def timed_ahead(fn, reps, stream):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(400_000 * reps)  # >= ~150 us of host time per call at <= 2.4 GHz
+    spin = getattr(torch.cuda, "_sleep", None)  # a private torch helper; without it the host is not ahead
+    if spin is not None:
+        with torch.cuda.stream(stream):
+            spin(400_000 * reps)  # >= ~150 us of host time per call at <= 2.4 GHz
     e0.record(stream)
     for _ in range(reps):
         fn()
